@@ -1,0 +1,178 @@
+"""Plain fp64 CPU oracle for exact attention (prefill) and paged decode.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module; only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library.
+
+What it computes is the plain definition of softmax attention as the
+"Attention Is the Bottleneck" page (samanvya.dev) writes it in "What attention
+costs": scores Q·Kᵀ times a scale, a row softmax, then the weighted sum of V.
+It follows the three-step textbook structure that page describes in the same
+section (scores, then probabilities, then the output), with host memory in the
+place of HBM: every row's full score vector is materialised.  There is no
+online softmax and no tiling here; the tiled, online form is what the GPU
+kernels do, and the pages state that it reaches this same result up to
+rounding ("FlashAttention: same math, different IO").
+
+Readings of points the pages leave open (kept identical in the kernels):
+  * scale multiplies Q·Kᵀ before the 0 / -inf mask is added; default 1/sqrt(d);
+  * LSE is the natural-log log-sum-exp of the scaled visible scores of a row;
+  * causal alignment is bottom-right: query i sits at key position i + Nk - Nq;
+  * a sliding window of width W lets a query see the W latest keys including
+    its own position (the "last W tokens" of the Sliding windows section);
+  * the document mask is causal inside each packed document (FlexAttention's
+    document masks, "Attention and matrix kernels" page, How it works);
+  * grouped-query heads are contiguous groups: kv head = q head // (Hq / Hkv)
+    (MQA and GQA section);
+  * a row that sees no key has output 0 and LSE -inf.
+
+Parity pins: see tests/test_oracle_pins.py (brute force in 50-digit
+arithmetic, closed forms, invariants, reductions and the worked example the
+page prints for the online-softmax recurrence).  No function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASKS = ("none", "causal", "window", "document")
+
+
+def from_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bit patterns (uint16) exactly to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Inputs as the oracle sees them: bf16 bit patterns or float32, widened exactly."""
+    if dtype == "bf16":
+        return from_bf16_bits(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def visibility(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None,
+               rows: np.ndarray | None = None) -> np.ndarray:
+    """Boolean matrix vis[i, j]: may query row i attend to key j?
+
+    Query i stands at key position pos = i + (Nk - Nq).
+      none      every key
+      causal    j <= pos
+      window    0 <= pos - j < window
+      document  j <= pos and key j lies in the same document as position pos
+    """
+    if mask not in MASKS:
+        raise ValueError(f"unknown mask {mask!r}")
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    pos = (i + (Nk - Nq))[:, None]
+    j = np.arange(Nk)[None, :]
+    if mask == "none":
+        return np.ones((i.size, Nk), dtype=bool)
+    if mask == "causal":
+        return j <= pos
+    if mask == "window":
+        if window < 1:
+            raise ValueError("window must be >= 1")
+        return (pos - j >= 0) & (pos - j < window)
+    off = np.asarray(doc_offsets, dtype=np.int64)
+    # document id of a key position: the last offset that is <= the position
+    doc_of_key = np.searchsorted(off, np.arange(Nk), side="right") - 1
+    pos_flat = pos[:, 0]
+    doc_of_pos = np.where(pos_flat >= 0,
+                          np.searchsorted(off, np.clip(pos_flat, 0, None), side="right") - 1, -1)
+    return (j <= pos) & (doc_of_key[None, :] == doc_of_pos[:, None])
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: str = "none",
+              window: int = 0, doc_offsets=None, rows=None, row_block: int = 1024):
+    """O = softmax(scale·Q·Kᵀ + mask)·V and LSE, in float64.
+
+    q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d] (float64).  Returns o with q's
+    shape (or [B, Hq, len(rows), d] when ``rows`` selects query rows) and
+    lse [B, Hq, Nq] (or [B, Hq, len(rows)]).  Rows are independent, so a row
+    subset is exact for the rows it lists.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    row_idx = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = row_idx.size
+    o = np.zeros((B, Hq, R, d), dtype=np.float64)
+    lse = np.full((B, Hq, R), -np.inf, dtype=np.float64)
+    if R == 0 or Nk == 0:
+        return o, lse
+    scale = float(scale)
+    for r0 in range(0, R, row_block):
+        sel = row_idx[r0:r0 + row_block]
+        vis = visibility(Nq, Nk, mask, window, doc_offsets, rows=sel)
+        any_vis = vis.any(axis=1)
+        for b in range(B):
+            for h in range(Hq):
+                hk = h // group
+                # step 1: scores for the full rows, then the additive mask
+                s = scale * (q[b, h, sel, :] @ k[b, hk].T)
+                s = np.where(vis, s, -np.inf)
+                # step 2: probabilities
+                m = np.max(s, axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                safe_l = np.where(l > 0, l, 1.0)
+                p = e / safe_l
+                # step 3: output and the log-sum-exp statistic
+                o[b, h, r0:r0 + sel.size] = p @ v[b, hk]
+                lse_blk = m[:, 0] + np.log(safe_l[:, 0])
+                lse[b, h, r0:r0 + sel.size] = np.where(any_vis, lse_blk, -np.inf)
+        o[:, :, r0:r0 + sel.size][:, :, ~any_vis] = 0.0
+    return o, lse
+
+
+def gather_sequence(pages: np.ndarray, block_table_row: np.ndarray, seq_len: int) -> np.ndarray:
+    """Contiguous [Hkv, seq_len, d] view of one sequence's paged K or V.
+
+    pages [num_pages, Hkv, page_size, d]; logical token t lives in physical
+    page block_table_row[t // page_size], slot t % page_size.
+    """
+    page_size = pages.shape[2]
+    t = np.arange(seq_len)
+    phys = np.asarray(block_table_row)[t // page_size]
+    return np.transpose(pages[phys, :, t % page_size, :], (1, 0, 2))
+
+
+def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                 seq_lens: np.ndarray, scale: float, seqs=None, dtype: str = "f64"):
+    """One-token decode over a paged KV cache, in float64.
+
+    q [S, Hq, d]; k_pages/v_pages [P, Hkv, page_size, d]; block_table
+    [S, max_pages]; seq_lens [S].  The single query of a sequence is its
+    newest token, so it sees every one of the sequence's ``seq_len`` cached
+    keys.  Returns o [S', Hq, d], lse [S', Hq] for the sequences ``seqs``
+    (default: all).  With ``dtype="bf16"`` q and the pages are raw bf16 bit
+    patterns, widened here one gathered sequence at a time.
+    """
+    q = to_f64(q, dtype) if dtype == "bf16" else np.asarray(q, dtype=np.float64)
+    S, Hq, d = q.shape
+    seqs = range(S) if seqs is None else list(seqs)
+    out_o = np.zeros((len(seqs), Hq, d), dtype=np.float64)
+    out_l = np.full((len(seqs), Hq), -np.inf, dtype=np.float64)
+    for n, s in enumerate(seqs):
+        L = int(seq_lens[s])
+        if L == 0:
+            continue
+        ks = gather_sequence(k_pages, block_table[s], L)
+        vs = gather_sequence(v_pages, block_table[s], L)
+        if dtype == "bf16":
+            ks, vs = from_bf16_bits(ks), from_bf16_bits(vs)
+        else:
+            ks, vs = ks.astype(np.float64), vs.astype(np.float64)
+        o, lse = attention(q[s][None, :, None, :], ks[None], vs[None], scale, "none")
+        out_o[n] = o[0, :, 0, :]
+        out_l[n] = lse[0, :, 0]
+    return out_o, out_l

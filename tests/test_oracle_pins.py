@@ -1,0 +1,355 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test fixes one property that the attention pages or plain mathematics
+state, so that a plausible slip in the oracle (a dropped term, a wrong sign
+or index, a transposed operand, an off-by-one mask) fails at least one test:
+
+  * brute force in 50-digit arithmetic on tiny inputs, for every mask kind;
+  * closed forms: constant V, identical keys, two keys, causal row 0;
+  * invariants: probabilities sum to one, key/value permutation;
+  * reductions: window >= N is causal, window 1 is the diagonal, the
+    document mask is causal attention run per document, GQA is MHA with the
+    KV heads repeated, bottom-right causal alignment when Nq < Nk;
+  * the worked example printed on the "Attention Is the Bottleneck" page
+    (section "FlashAttention: same math, different IO"): the running-max /
+    running-sum form agrees with the full softmax to rounding noise;
+  * the split-KV log-sum-exp combine of the Flash-Decoding section.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- brute force
+
+def _visible_keys(i, Nq, Nk, mask, window, offsets):
+    """Visible key set of query row i, enumerated rule by rule."""
+    pos = i + Nk - Nq
+    if mask == "none":
+        return list(range(Nk))
+    if mask == "causal":
+        return [j for j in range(Nk) if j <= pos]
+    if mask == "window":
+        return [j for j in range(Nk) if pos - window < j <= pos]
+    # document: scan the offsets for the document holding position pos
+    if pos < 0:
+        return []
+    start = None
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        if a <= pos < b:
+            start = a
+    return [j for j in range(Nk) if start <= j <= pos]
+
+
+def _brute(q, k, v, scale, mask, window=0, offsets=None):
+    mpmath.mp.dps = 50
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros(q.shape)
+    L = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            for i in range(Nq):
+                keys = _visible_keys(i, Nq, Nk, mask, window, offsets)
+                if not keys:
+                    continue
+                s = {j: mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, h, i, c]) * mpmath.mpf(k[b, hk, j, c])
+                                                        for c in range(d)) for j in keys}
+                w = {j: mpmath.exp(s[j]) for j in keys}
+                tot = mpmath.fsum(w.values())
+                for c in range(d):
+                    O[b, h, i, c] = float(mpmath.fsum(w[j] * mpmath.mpf(v[b, hk, j, c]) for j in keys) / tot)
+                L[b, h, i] = float(mpmath.log(tot))
+    return O, L
+
+
+@pytest.mark.parametrize("mask,window,offsets,Nq,Nk", [
+    ("none", 0, None, 5, 6),
+    ("causal", 0, None, 6, 6),
+    ("causal", 0, None, 3, 6),      # bottom-right alignment, Nq < Nk
+    ("causal", 0, None, 6, 4),      # Nq > Nk: the first rows see nothing
+    ("window", 1, None, 6, 6),
+    ("window", 2, None, 6, 6),
+    ("window", 3, None, 4, 6),
+    ("document", 0, [0, 2, 5, 6], 6, 6),
+    ("document", 0, [0, 1, 6], 6, 6),
+])
+def test_brute_force_tiny(mask, window, offsets, Nq, Nk):
+    B, Hq, Hkv, d = 1, 4, 2, 3
+    q, k, v = rnd(1, B, Hq, Nq, d), rnd(2, B, Hkv, Nk, d), rnd(3, B, Hkv, Nk, d)
+    scale = 0.7
+    o, lse = oracle.attention(q, k, v, scale, mask, window, offsets)
+    ob, lb = _brute(q, k, v, scale, mask, window, offsets)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    fin = np.isfinite(lb)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-13)
+    assert np.all(o[~fin] == 0.0)
+
+
+# --------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 5)])
+def test_probabilities_sum_to_one(mask, window):
+    # With V the identity matrix, each output row is the probability row itself.
+    N = 24
+    q, k = rnd(4, 1, 2, N, 8), rnd(5, 1, 2, N, 8)
+    v = np.broadcast_to(np.eye(N), (1, 2, N, N)).copy()
+    # head dim of V must match q's for the oracle; pad q and k with zeros instead
+    qp = np.concatenate([q, np.zeros((1, 2, N, N - 8))], axis=-1)
+    kp = np.concatenate([k, np.zeros((1, 2, N, N - 8))], axis=-1)
+    p, _ = oracle.attention(qp, kp, v, 0.5, mask, window)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    assert np.all(p >= 0)
+    vis = oracle.visibility(N, N, mask, window)
+    assert np.all(p[0, 0][~vis] == 0.0)
+    assert np.all(p[0, 0][vis] > 0.0)
+
+
+@pytest.mark.parametrize("mask,window,offsets", [("none", 0, None), ("causal", 0, None),
+                                                 ("window", 3, None), ("document", 0, [0, 7, 9, 20])])
+def test_constant_v_gives_constant_output(mask, window, offsets):
+    N, d = 20, 6
+    c = rnd(6, d)
+    v = np.broadcast_to(c, (1, 2, N, d)).copy()
+    o, _ = oracle.attention(rnd(7, 1, 4, N, d), rnd(8, 1, 2, N, d), v, 1.3, mask, window, offsets)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-13)
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 4)])
+def test_identical_keys_give_mean_of_visible_values(mask, window):
+    N, d, scale = 16, 5, 0.9
+    q = rnd(9, 1, 1, N, d)
+    kk = rnd(10, d)
+    k = np.broadcast_to(kk, (1, 1, N, d)).copy()
+    v = rnd(11, 1, 1, N, d)
+    o, lse = oracle.attention(q, k, v, scale, mask, window)
+    vis = oracle.visibility(N, N, mask, window)
+    for i in range(N):
+        idx = np.nonzero(vis[i])[0]
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, idx].mean(axis=0), atol=1e-13)
+        assert lse[0, 0, i] == pytest.approx(scale * q[0, 0, i] @ kk + math.log(idx.size), abs=1e-13)
+    # Q = 0: uniform weights whatever the keys are, LSE = ln(#visible)
+    o0, l0 = oracle.attention(np.zeros_like(q), rnd(12, 1, 1, N, d), v, scale, mask, window)
+    for i in range(N):
+        idx = np.nonzero(vis[i])[0]
+        np.testing.assert_allclose(o0[0, 0, i], v[0, 0, idx].mean(axis=0), atol=1e-13)
+        assert l0[0, 0, i] == pytest.approx(math.log(idx.size), abs=1e-13)
+
+
+def test_two_keys_is_a_logistic_blend():
+    d, scale = 7, 0.4
+    q, k, v = rnd(13, 1, 1, 3, d), rnd(14, 1, 1, 2, d), rnd(15, 1, 1, 2, d)
+    o, lse = oracle.attention(q, k, v, scale)
+    for i in range(3):
+        s0, s1 = scale * q[0, 0, i] @ k[0, 0, 0], scale * q[0, 0, i] @ k[0, 0, 1]
+        w = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+        np.testing.assert_allclose(o[0, 0, i], w * v[0, 0, 0] + (1 - w) * v[0, 0, 1], atol=1e-13)
+        assert lse[0, 0, i] == pytest.approx(max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1))), abs=1e-13)
+
+
+def test_causal_row_zero_copies_first_value():
+    q, k, v = rnd(16, 2, 3, 9, 4), rnd(17, 2, 3, 9, 4), rnd(18, 2, 3, 9, 4)
+    o, lse = oracle.attention(q, k, v, 0.8, "causal")
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.8 * np.einsum("bhc,bhc->bh", q[:, :, 0], k[:, :, 0]),
+                               atol=1e-14)
+
+
+def test_large_scale_tends_to_hard_max():
+    q, k, v = rnd(19, 1, 1, 6, 4), rnd(20, 1, 1, 10, 4), rnd(21, 1, 1, 10, 4)
+    o, _ = oracle.attention(q, k, v, 1e3)
+    best = np.argmax(q[0, 0] @ k[0, 0].T, axis=1)
+    np.testing.assert_allclose(o[0, 0], v[0, 0, best], atol=1e-9)
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_unmasked_permutation_invariance():
+    N, d = 33, 8
+    q, k, v = rnd(22, 1, 2, 11, d), rnd(23, 1, 2, N, d), rnd(24, 1, 2, N, d)
+    perm = np.random.default_rng(25).permutation(N)
+    o1, l1 = oracle.attention(q, k, v, 0.35)
+    o2, l2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.35)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+    # permuting only V must change the output (the pairing of k and v matters)
+    o3, _ = oracle.attention(q, k, v[:, :, perm], 0.35)
+    assert np.abs(o3 - o1).max() > 1e-3
+
+
+def test_row_subset_matches_full():
+    q, k, v = rnd(26, 1, 2, 40, 8), rnd(27, 1, 2, 40, 8), rnd(28, 1, 2, 40, 8)
+    rows = np.array([0, 5, 17, 39])
+    of, lf = oracle.attention(q, k, v, 0.3, "causal")
+    os_, ls = oracle.attention(q, k, v, 0.3, "causal", rows=rows)
+    np.testing.assert_array_equal(os_, of[:, :, rows])
+    np.testing.assert_array_equal(ls, lf[:, :, rows])
+
+
+# ----------------------------------------------------------------- reductions
+
+def test_window_reductions():
+    N, d = 30, 6
+    q, k, v = rnd(29, 1, 2, N, d), rnd(30, 1, 2, N, d), rnd(31, 1, 2, N, d)
+    oc, lc = oracle.attention(q, k, v, 0.5, "causal")
+    ow, lw = oracle.attention(q, k, v, 0.5, "window", window=N)
+    np.testing.assert_array_equal(ow, oc)
+    np.testing.assert_array_equal(lw, lc)
+    o1, l1 = oracle.attention(q, k, v, 0.5, "window", window=1)
+    assert np.array_equal(o1, v)
+    np.testing.assert_allclose(l1, 0.5 * np.einsum("bhnc,bhnc->bhn", q, k), atol=1e-14)
+
+
+def test_document_mask_is_causal_per_document():
+    offsets = [0, 5, 6, 19, 32]
+    N, d = 32, 6
+    q, k, v = rnd(32, 1, 4, N, d), rnd(33, 1, 2, N, d), rnd(34, 1, 2, N, d)
+    o, lse = oracle.attention(q, k, v, 0.6, "document", doc_offsets=offsets)
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        od, ld = oracle.attention(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], 0.6, "causal")
+        np.testing.assert_allclose(o[:, :, a:b], od, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, a:b], ld, atol=1e-13)
+    # a single document over everything is the causal mask
+    o1, l1 = oracle.attention(q, k, v, 0.6, "document", doc_offsets=[0, N])
+    oc, lc = oracle.attention(q, k, v, 0.6, "causal")
+    np.testing.assert_array_equal(o1, oc)
+    np.testing.assert_array_equal(l1, lc)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    Hq, Hkv, N, d = 8, 2, 12, 4
+    q, k, v = rnd(35, 2, Hq, N, d), rnd(36, 2, Hkv, N, d), rnd(37, 2, Hkv, N, d)
+    o, lse = oracle.attention(q, k, v, 0.5, "causal")
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    om, lm = oracle.attention(q, kr, vr, 0.5, "causal")
+    np.testing.assert_array_equal(o, om)
+    np.testing.assert_array_equal(lse, lm)
+    # the interleaved grouping (kv head = q head % Hkv) is a different result
+    ki, vi = np.tile(k, (1, Hq // Hkv, 1, 1)), np.tile(v, (1, Hq // Hkv, 1, 1))
+    oi, _ = oracle.attention(q, ki, vi, 0.5, "causal")
+    assert np.abs(oi - o).max() > 1e-3
+
+
+def test_bottom_right_alignment():
+    # with Nq < Nk the last query row sees every key, like an unmasked row
+    Nq, Nk, d = 4, 10, 5
+    q, k, v = rnd(38, 1, 1, Nq, d), rnd(39, 1, 1, Nk, d), rnd(40, 1, 1, Nk, d)
+    oc, lc = oracle.attention(q, k, v, 0.7, "causal")
+    on, ln = oracle.attention(q, k, v, 0.7, "none")
+    np.testing.assert_allclose(oc[:, :, -1], on[:, :, -1], atol=1e-14)
+    # and row i sees exactly the first i + 1 + (Nk - Nq) keys
+    for i in range(Nq):
+        n = i + 1 + Nk - Nq
+        oi, li = oracle.attention(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], 0.7, "none")
+        np.testing.assert_allclose(oc[:, :, i], oi[:, :, 0], atol=1e-14)
+        np.testing.assert_allclose(lc[:, :, i], li[:, :, 0], atol=1e-14)
+
+
+def test_rows_that_see_nothing():
+    Nq, Nk = 6, 3
+    q, k, v = rnd(41, 1, 1, Nq, 4), rnd(42, 1, 1, Nk, 4), rnd(43, 1, 1, Nk, 4)
+    o, lse = oracle.attention(q, k, v, 1.0, "causal")
+    assert np.all(o[0, 0, :3] == 0) and np.all(np.isneginf(lse[0, 0, :3]))
+    assert np.all(np.isfinite(lse[0, 0, 3:]))
+    o, lse = oracle.attention(q, k[:, :, :0], v[:, :, :0], 1.0, "none")
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ------------------------------------------------ the page's worked example
+
+def _online_softmax_one_query(q, K, V, block):
+    """Running max / running sum over key blocks, written out for one query."""
+    scale = 1.0 / math.sqrt(q.shape[0])
+    run_max, run_sum = -math.inf, 0.0
+    acc = np.zeros(V.shape[1])
+    for a in range(0, K.shape[0], block):
+        s = (K[a:a + block] @ q) * scale
+        new_max = max(run_max, float(s.max()))
+        shrink = math.exp(run_max - new_max)          # 0 on the first block
+        w = np.exp(s - new_max)
+        run_sum = run_sum * shrink + w.sum()
+        acc = acc * shrink + w @ V[a:a + block]
+        run_max = new_max
+    return acc / run_sum
+
+
+def test_worked_example_online_softmax_matches_oracle():
+    g = json.load(open(os.path.join(GOLDEN, "online_softmax_worked_example.json")))
+    rng = np.random.default_rng(g["seed"])
+    q = rng.standard_normal(g["d"])
+    K = rng.standard_normal((g["n_keys"], g["d"]))
+    V = rng.standard_normal((g["n_keys"], g["d"]))
+    tiled = _online_softmax_one_query(q, K, V, g["block"])
+    o, _ = oracle.attention(q[None, None, None, :], K[None, None], V[None, None], 1.0 / math.sqrt(g["d"]))
+    diff = np.abs(o[0, 0, 0] - tiled).max()
+    assert diff < 100 * g["printed_max_abs_diff"]
+    # and every block size, including ragged tails, gives the same answer
+    for block in (1, 7, 64, 1000, 4096):
+        assert np.abs(_online_softmax_one_query(q, K, V, block) - o[0, 0, 0]).max() < 1e-14
+
+
+# ------------------------------------------------ split-KV log-sum-exp combine
+
+def test_split_lse_combine_equals_whole():
+    N, d = 100, 8
+    q, k, v = rnd(44, 1, 3, 1, d), rnd(45, 1, 3, N, d), rnd(46, 1, 3, N, d)
+    o, lse = oracle.attention(q, k, v, 0.4)
+    cuts = [0, 13, 14, 50, 99, 100]
+    parts = [oracle.attention(q, k[:, :, a:b], v[:, :, a:b], 0.4) for a, b in zip(cuts[:-1], cuts[1:])]
+    L = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+    O = sum(np.exp(p[1] - L)[..., None] * p[0] for p in parts)
+    np.testing.assert_allclose(L, lse, atol=1e-14)
+    np.testing.assert_allclose(O, o, atol=1e-14)
+
+
+# ---------------------------------------------------------------- paged decode
+
+def test_paged_decode_equals_contiguous_attention():
+    S, Hq, Hkv, d, P = 3, 4, 2, 8, 16
+    lens = [1, 37, 64]
+    rng = np.random.default_rng(47)
+    q = rng.standard_normal((S, Hq, d))
+    conts = [(rng.standard_normal((Hkv, n, d)), rng.standard_normal((Hkv, n, d))) for n in lens]
+    npages = sum(-(-n // P) for n in lens)
+    perm = rng.permutation(npages)
+    kp = np.full((npages, Hkv, P, d), np.nan)
+    vp = np.full((npages, Hkv, P, d), np.nan)
+    bt = np.full((S, 4), -1, dtype=np.int32)
+    g = 0
+    for s, n in enumerate(lens):
+        for p in range(-(-n // P)):
+            phys = perm[g]
+            g += 1
+            bt[s, p] = phys
+            m = min(P, n - p * P)
+            kp[phys, :, :m] = conts[s][0][:, p * P:p * P + m]
+            vp[phys, :, :m] = conts[s][1][:, p * P:p * P + m]
+    o, lse = oracle.paged_decode(q, kp, vp, bt, np.array(lens), 0.3)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))   # NaN tails never read
+    for s, n in enumerate(lens):
+        oc, lc = oracle.attention(q[s][None, :, None, :], conts[s][0][None], conts[s][1][None], 0.3)
+        np.testing.assert_allclose(o[s], oc[0, :, 0], atol=1e-14)
+        np.testing.assert_allclose(lse[s], lc[0, :, 0], atol=1e-14)
+
+
+def test_generated_decode_layout_matches_oracle_gather():
+    c = workloads.make_decode(4, 8, 2, 16, len_min=5, len_max=70, seed=3, tail_fill="nan")
+    o, lse = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                 c["scale"], dtype="bf16")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
