@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal bf16 prefill (B=4, Hq=Hkv=16, N=2048, d=128, the
+headline workload) followed by one paged decode (64 sequences, Hq=32, Hkv=8,
+d=128, context lengths uniform in [1024, 32768], 16-token pages, seeded
+random page placement).  Inputs are seeded synthetic data, generated on the
+host, copied once and resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  `value` is the prefill's algorithmic TFLOP/s
+(4·d·B·Hq·visible pairs per call ÷ the kernel's mean duration from HIP events
+on the launch stream); the decode's algorithmic HBM GB/s is reported beside
+it.  `cpu_baseline` is the fp64 numpy oracle timed on this host over a bounded
+sample of the same prefill workload.
+
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
+
+turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+`bench.py --pmc-pass` into profiles/hbm_traffic.json.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0         # HBM3E
+PREFILL_CONFIG = "c2_causal_b4h16n2048"
+DECODE_CONFIG = "c5_paged_decode_64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "exact_io_aware_fwd_amd", "csrc")
+COPY_BYTES = 1 << 30          # known-size copy used to calibrate the HBM byte counters
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- work accounting
+
+def visible_pairs(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None) -> int:
+    """Number of (query, key) pairs a mask lets through, per (batch, head)."""
+    i = np.arange(Nq, dtype=np.int64)
+    pos = i + (Nk - Nq)
+    if mask == "none":
+        return Nq * Nk
+    hi = np.minimum(pos, Nk - 1)
+    if mask == "causal":
+        lo = np.zeros_like(pos)
+    elif mask == "window":
+        lo = np.maximum(pos - window + 1, 0)
+    elif mask == "document":
+        off = np.asarray(doc_offsets, dtype=np.int64)
+        lo = off[np.clip(np.searchsorted(off, np.maximum(pos, 0), side="right") - 1, 0, len(off) - 2)]
+    else:
+        raise ValueError(mask)
+    cnt = np.where(pos >= 0, hi - lo + 1, 0)
+    return int(np.clip(cnt, 0, None).sum())
+
+
+def prefill_flops(c: dict) -> int:
+    return 4 * c["d"] * c["B"] * c["Hq"] * visible_pairs(c["Nq"], c["Nk"], c["mask"], c["window"], c["doc_offsets"])
+
+
+def prefill_bytes(c: dict) -> int:
+    el = 2 if c["dtype"] == "bf16" else 4
+    q = c["B"] * c["Hq"] * c["Nq"] * c["d"] * el
+    kv = 2 * c["B"] * c["Hkv"] * c["Nk"] * c["d"] * el
+    return q + kv + q + c["B"] * c["Hq"] * c["Nq"] * 4
+
+
+def decode_bytes(c: dict) -> int:
+    """HBM bytes a paged decode must move: the cache it reads, q, o, lse and the index data."""
+    lens = c["seq_lens"].astype(np.int64)
+    S, Hq, Hkv, d = c["num_seqs"], c["Hq"], c["Hkv"], c["d"]
+    kv = int(lens.sum()) * Hkv * d * 2 * 2
+    pages = int((-(-lens // c["page_size"])).sum())
+    return kv + 2 * S * Hq * d * 2 + S * Hq * 4 + pages * 4 + S * 4
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_key: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this workload or the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel_key)
+    if not k or k.get("workload") != workload:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+# -------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(c: dict, budget_s: float) -> dict:
+    """The fp64 oracle, as it is, on whole (batch, head) slices of the prefill
+    workload until the time budget is spent; TFLOP/s of algorithmic work."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    per_head = 4 * c["d"] * visible_pairs(c["Nq"], c["Nk"], c["mask"], c["window"], c["doc_offsets"])
+    g = c["Hq"] // c["Hkv"]
+    heads = [(b, h) for b in range(c["B"]) for h in range(c["Hq"])]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        hk = h // g
+        q = oracle.to_f64(c["q"][b:b + 1, h:h + 1], c["dtype"])
+        k = oracle.to_f64(c["k"][b:b + 1, hk:hk + 1], c["dtype"])
+        v = oracle.to_f64(c["v"][b:b + 1, hk:hk + 1], c["dtype"])
+        oracle.attention(q, k, v, c["scale"], c["mask"], c["window"], c["doc_offsets"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done * per_head / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{PREFILL_CONFIG}: {done} of {len(heads)} (batch, head) slices, all {c['Nq']} rows each, "
+                      f"{el:.1f} s fp64 numpy"}
+
+
+# ------------------------------------------------------------------- GPU run
+
+def to_dev(x: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-config", default=PREFILL_CONFIG)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="short run for counter collection: a few steps plus one known-size copy")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
+                                   "this build (--gpus must be 1)"}))
+        return 2
+
+    import torch
+    from exact_io_aware_fwd_amd import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size
+
+    torch.cuda.set_device(0)
+    log(f"generating inputs ({args.prefill_config}, {DECODE_CONFIG})")
+    pc = workloads.prefill_config(args.prefill_config)
+    dc = workloads.decode_config(DECODE_CONFIG)
+    q, k, v = to_dev(pc["q"]), to_dev(pc["k"]), to_dev(pc["v"])
+    doc = torch.from_numpy(pc["doc_offsets"]).cuda() if pc["doc_offsets"] is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.float32, device="cuda")
+    dq, dk, dv = to_dev(dc["q"]), to_dev(dc["k_pages"]), to_dev(dc["v_pages"])
+    bt = torch.from_numpy(dc["block_table"]).cuda()
+    sl = torch.from_numpy(dc["seq_lens"]).cuda()
+    do = torch.empty_like(dq)
+    dl = torch.empty((dc["num_seqs"], dc["Hq"]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(attn_paged_decode_workspace_size(dc["num_seqs"], dc["Hq"], dc["d"], dc["max_seq_len"]),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    def prefill():
+        attn_fwd(q, k, v, scale=pc["scale"], mask=pc["mask"], window=pc["window"], doc_offsets=doc, out=o, lse=lse)
+
+    def decode():
+        attn_paged_decode(dq, dk, dv, bt, sl, max_seq_len=dc["max_seq_len"], scale=dc["scale"], workspace=ws,
+                          out=do, lse=dl)
+
+    if args.pmc_pass:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        for _ in range(3):
+            prefill()
+            decode()
+        torch.cuda.synchronize()
+        log("pmc pass done")
+        return 0
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+    log(f"warmup done ({W} steps)")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        evs[i][0].record()
+        prefill()
+        evs[i][1].record()
+        decode()
+        evs[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = start.elapsed_time(end) / K
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_mean, dec_mean = float(np.mean(pre_ms)), float(np.mean(dec_ms))
+    log(f"timed {K} steps: {step_ms:.3f} ms/step (wall {wall:.2f} s); prefill {pre_mean*1e3:.1f} us, "
+        f"decode {dec_mean*1e3:.1f} us")
+
+    flops = prefill_flops(pc)
+    tflops = flops / (pre_mean * 1e-3) / 1e12
+    dbytes = decode_bytes(dc)
+    gbs = dbytes / (dec_mean * 1e-3) / 1e9
+    pkey = f"prefill_bf16_kernel<{pc['d']}>"
+    ptraffic = measured_traffic(pkey, args.prefill_config)
+    dtraffic = measured_traffic("decode_split_kernel<128>", DECODE_CONFIG)
+
+    result = {
+        "metric": "attn fwd TFLOP/s (% bf16 MFMA peak) causal prefill; paged decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.prefill_config} (B{pc['B']} Hq{pc['Hq']} Hkv{pc['Hkv']} N{pc['Nq']} d{pc['d']} "
+                        f"{pc['mask']}) + {DECODE_CONFIG} (64 seqs, Hq32 Hkv8 d128, 16-token pages, "
+                        f"{int(dc['seq_lens'].sum())} cached tokens)",
+            "prefill_flop_per_call": flops,
+            "prefill_us": round(pre_mean * 1e3, 2),
+            "decode_bytes_per_call": dbytes,
+            "decode_us": round(dec_mean * 1e3, 2),
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": ptraffic,
+            "kernel": pkey, "algorithmic_bytes": prefill_bytes(pc),
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s", "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
+                         "kernel": "decode_split_kernel<128> + decode_combine_kernel<128> (one call)"},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(pc, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+# ------------------------------------------------------- counter summaries
+
+def _read_counters(d: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3 --pmc run."""
+    import csv
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    vals: dict = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (row.get("Dispatch_Id"), row.get("Kernel_Name"))
+            vals.setdefault(key, 0.0)
+            vals[key] += float(row["Counter_Value"])
+    per_kernel: dict = {}
+    for (_, name), v in vals.items():
+        per_kernel.setdefault(name, []).append(v)
+    return {k: float(np.mean(v)) for k, v in per_kernel.items()}
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
+    fetch = _read_counters(fetch_dir, "FETCH_SIZE")
+    write = _read_counters(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy:
+        raise SystemExit("copy kernel not found in the FETCH_SIZE run")
+    ck = max(copy, key=lambda k: fetch[k])
+    f_factor = (COPY_BYTES / 1024.0) / fetch[ck]
+    w_factor = (COPY_BYTES / 1024.0) / write.get(ck, float("nan"))
+    out = {"source_sha256": source_digest(), "copy_kernel": ck, "copy_bytes": COPY_BYTES,
+           "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
+    for name in fetch:
+        short = None
+        for tag in ("prefill_bf16_kernel<128>", "prefill_bf16_kernel<64>", "decode_split_kernel<128>",
+                    "decode_combine_kernel<128>"):
+            if tag in name:
+                short = tag
+        if short is None:
+            continue
+        wl = PREFILL_CONFIG if short.startswith("prefill") else DECODE_CONFIG
+        out["kernels"][short] = {"workload": wl, "fetch_kib_raw": fetch[name], "write_kib_raw": write.get(name),
+                                 "fetch_bytes": fetch[name] * 1024 * f_factor,
+                                 "write_bytes": write.get(name, 0.0) * 1024 * w_factor}
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

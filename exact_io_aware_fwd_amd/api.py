@@ -1,0 +1,108 @@
+"""Python binding over the C ABI (same names, torch tensors in, torch tensors out).
+
+The functions only check tensor metadata, allocate outputs with torch and pass
+raw device pointers plus torch's current HIP stream to the library; every
+step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.ATTN_DTYPE_BF16, torch.float32: _lib.ATTN_DTYPE_F32}
+
+
+def ctypes_ptr(t: torch.Tensor):
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None) -> _lib.AttnMask:
+    _need(mask in _lib.MASK_KINDS, f"unknown mask {mask!r}")
+    m = _lib.AttnMask()
+    m.kind = _lib.MASK_KINDS[mask]
+    m.window = int(window) if mask == "window" else 0
+    if mask == "document":
+        _need(doc_offsets is not None and doc_offsets.dtype == torch.int32 and doc_offsets.is_cuda
+              and doc_offsets.is_contiguous(), "document mask needs int32 device doc_offsets")
+        m.doc_offsets = doc_offsets.data_ptr()
+        m.num_docs = doc_offsets.numel() - 1
+    else:
+        m.doc_offsets = None
+        m.num_docs = 0
+    return m
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float | None = None,
+             mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None, with_lse: bool = True,
+             stream=None):
+    """Attention forward: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> (o [B,Hq,Nq,d], lse [B,Hq,Nq] fp32)."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-d [B, H, N, d]")
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "dtype must be bf16 or fp32, same for q/k/v")
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous device tensors")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape == v.shape and k.shape[0] == B and k.shape[3] == d, "k/v shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    m = make_mask(mask, window, doc_offsets)
+    st = _lib.lib().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
+                             None if lse is None else ctypes_ptr(lse),
+                             B, Hq, Hkv, Nq, Nk, d, float(scale), m, _DTYPES[q.dtype], _stream(stream))
+    _lib.check(st)
+    return out, lse
+
+
+def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, d: int, max_seq_len: int) -> int:
+    return int(_lib.lib().attn_paged_decode_workspace_size(num_seqs, Hq, d, max_seq_len))
+
+
+def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
+                      scale: float | None = None, workspace: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      with_lse: bool = True, stream=None):
+    """Paged decode: q [S,Hq,d], pages [P,Hkv,16,d] -> (o [S,Hq,d] bf16, lse [S,Hq] fp32)."""
+    _need(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad shapes")
+    _need(q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16,
+          "paged decode is bf16")
+    _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k_pages, v_pages, block_table, seq_lens)),
+          "inputs must be contiguous device tensors")
+    S, Hq, d = q.shape
+    _, Hkv, page_size, _ = k_pages.shape
+    _need(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,), "index shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_paged_decode_workspace_size(S, Hq, d, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    st = _lib.lib().attn_paged_decode(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
+                                      ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(out),
+                                      None if lse is None else ctypes_ptr(lse),
+                                      S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
+                                      float(scale), ctypes_ptr(workspace), workspace.numel(), _stream(stream))
+    _lib.check(st)
+    return out, lse

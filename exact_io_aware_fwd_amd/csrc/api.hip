@@ -1,0 +1,122 @@
+// C ABI of the attention library: argument checks, launch geometry, status codes.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/exact_attn.h"
+#include "common.hpp"
+
+namespace xattn {
+int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+int launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
+}  // namespace xattn
+
+#include "decode_params.hpp"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "HIP error";
+
+constexpr long long kMaxSeq = 1LL << 28;     // keeps every row / position index in int32
+constexpr long long kMaxGrid = 1LL << 24;    // workgroups per launch (x 256 threads < 2^32)
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error: %s", hipGetErrorString(e));
+    return ATTN_ERR_HIP;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+}  // namespace
+
+extern "C" const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case ATTN_ERR_HIP: return g_hip_msg;
+        default: return "unknown status";
+    }
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        attn_mask mask, int dtype, hipStream_t stream) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind < ATTN_MASK_NONE || mask.kind > ATTN_MASK_DOCUMENT) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_DOCUMENT && (mask.num_docs < 1 || mask.doc_offsets == nullptr))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
+    if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * Hq * Nq == 0) return ATTN_OK;  // nothing to write
+    if (q == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+    if (Nk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARGUMENT;
+    const long long tiles = (Nq + 127) / 128;
+    if ((long long)B * Hq * tiles > kMaxGrid) return ATTN_ERR_UNSUPPORTED;
+
+    xattn::PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+    p.group = Hq / Hkv;
+    p.scale_log2 = scale * xattn::kLog2e;
+    p.mask_kind = mask.kind;
+    p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? (mask.window < Nk ? mask.window : (Nk > 0 ? Nk : 1)) : 0;
+    p.doc_offsets = mask.kind == ATTN_MASK_DOCUMENT ? mask.doc_offsets : nullptr;
+    p.num_docs = mask.kind == ATTN_MASK_DOCUMENT ? mask.num_docs : 0;
+    p.num_q_tiles = (int)tiles;
+
+    if (dtype == ATTN_DTYPE_BF16)
+        xattn::launch_prefill_bf16(p, d, stream);
+    else
+        xattn::launch_prefill_f32(p, d, stream);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, int max_seq_len) {
+    if (num_seqs < 0 || Hq < 0 || max_seq_len < 0 || (d != 64 && d != 128)) return 0;
+    return xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len);
+}
+
+extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 void* o, float* lse,
+                                 int num_seqs, int Hq, int Hkv, int d, int page_size,
+                                 int max_pages_per_seq, int max_seq_len, float scale,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_seqs < 0 || Hq < 0 || Hkv < 0 || d < 0 || max_pages_per_seq < 0 || max_seq_len < 0)
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)max_pages_per_seq * page_size < max_seq_len) return ATTN_ERR_INVALID_ARGUMENT;
+    if (max_seq_len > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * Hq == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || seq_lens == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
+    if (max_seq_len > 0 && (k_pages == nullptr || v_pages == nullptr || block_table == nullptr))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    const size_t need = xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
+    const long long splits = (max_seq_len + xattn::kSplitTokens - 1) / xattn::kSplitTokens;
+    if ((long long)num_seqs * Hkv * (splits > 0 ? splits : 1) > kMaxGrid) return ATTN_ERR_UNSUPPORTED;
+
+    xattn::DecodeParams p;
+    p.q = (const uint16_t*)q; p.kp = (const uint16_t*)k_pages; p.vp = (const uint16_t*)v_pages;
+    p.block_table = block_table; p.seq_lens = seq_lens;
+    p.o = (uint16_t*)o; p.lse = lse;
+    p.num_seqs = num_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+    p.max_pages = max_pages_per_seq; p.max_splits = 0;
+    p.scale_log2 = scale * xattn::kLog2e;
+    p.ws_o = nullptr; p.ws_lse = nullptr;
+    xattn::launch_decode(p, d, max_seq_len, workspace, stream);
+    return hip_status(hipGetLastError());
+}

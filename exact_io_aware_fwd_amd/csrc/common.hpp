@@ -1,0 +1,127 @@
+// Shared device-side definitions for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, workgroups dealt round-robin
+
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 3 };
+
+// Arguments of one prefill launch (already validated on the host).
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk;
+    int group;          // Hq / Hkv
+    float scale_log2;   // scale * log2(e): scores go straight to the base-2 domain
+    int mask_kind;
+    int window;         // clamped to [1, Nk] on the host
+    const int32_t* doc_offsets;
+    int num_docs;
+    int num_q_tiles;
+};
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// First key position of the document that holds key position `pos` (pos >= 0).
+__device__ __forceinline__ int doc_start(const int32_t* off, int num_docs, int pos) {
+    int lo = 0, hi = num_docs - 1;  // answer t in [0, num_docs-1] with off[t] <= pos
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= pos) lo = mid; else hi = mid - 1;
+    }
+    return off[lo];
+}
+
+// Visible keys of query row i form one interval [lo, hi] (inclusive) for every
+// mask kind; an empty row has lo > hi.  Query i sits at key position
+// pos = i + Nk - Nq.  Both ends are non-decreasing in i, which is what lets a
+// tile of rows bound its key range by its first and last row.
+__device__ __forceinline__ void row_interval(const PrefillParams& p, int i, int& lo, int& hi) {
+    if (i < 0 || i >= p.Nq) { lo = p.Nk; hi = -1; return; }
+    const int pos = i + p.Nk - p.Nq;
+    if (p.mask_kind == kMaskNone) { lo = 0; hi = p.Nk - 1; return; }
+    hi = pos < p.Nk - 1 ? pos : p.Nk - 1;
+    if (pos < 0) { lo = 0; hi = -1; return; }
+    if (p.mask_kind == kMaskCausal) {
+        lo = 0;
+    } else if (p.mask_kind == kMaskWindow) {
+        lo = pos - p.window + 1;
+        lo = lo > 0 ? lo : 0;
+    } else {
+        lo = doc_start(p.doc_offsets, p.num_docs, pos);
+    }
+}
+
+// Workgroup id -> (b*Hkv + kv head, q tile, head within the group).
+// Tiles are issued heaviest first (descending q tile: under causal-type masks
+// later tiles see more keys).  When the (batch, kv head) pairs divide evenly
+// over the dies, every die gets whole pairs, so the K/V of a pair stays in
+// that die's own L2.
+__device__ __forceinline__ void decode_work(int id, int nbk, int nqt, int group,
+                                            int& bk, int& qt, int& g) {
+    int qrev, r;
+    if (nbk % kNumXcd == 0) {
+        const int x = id % kNumXcd, u = id / kNumXcd;
+        const int bpx = nbk / kNumXcd;
+        qrev = u / (bpx * group);
+        r = u % (bpx * group);
+        bk = x * bpx + r / group;
+    } else {
+        qrev = id / (nbk * group);
+        r = id % (nbk * group);
+        bk = r / group;
+    }
+    g = r % group;
+    qt = nqt - 1 - qrev;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 f = {a, b};
+    bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                           false);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+}  // namespace xattn

@@ -1,0 +1,157 @@
+/*
+ * exact_attn.h — C ABI of the exact, IO-aware attention forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is softmax attention, O = softmax(scale * Q K^T + mask) V, as
+ * defined on the "Attention Is the Bottleneck" page (samanvya.dev), section
+ * "What attention costs".  It is evaluated tile by tile with an online
+ * softmax (a running row maximum and row sum, with the partial output
+ * rescaled whenever the maximum grows), as that page describes in
+ * "FlashAttention: same math, different IO", so no N x N score matrix is ever
+ * written to device memory.  The result equals the plain definition up to
+ * floating-point rounding order.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing and keeps no per-call state.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no
+ *     entry point synchronises the host.
+ *   - Arguments are checked before any HIP call; a failing check returns an
+ *     error status and enqueues nothing.  The contents of device-resident
+ *     index arrays (document offsets, block tables, sequence lengths) are a
+ *     caller contract and are not checked.
+ *   - Tensors are dense and row-major with the head dimension fastest, and
+ *     every base pointer must be 16-byte aligned.
+ *   - Return value: an attn_status.  attn_status_string() turns it into
+ *     text; for ATTN_ERR_HIP it also reports the HIP error of the failing
+ *     launch on the calling thread.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, bad mask field ... */
+    ATTN_ERR_UNSUPPORTED = 2,         /* valid request this build does not implement (e.g. d) */
+    ATTN_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below attn_paged_decode_workspace_size */
+    ATTN_ERR_HIP = 4                  /* a HIP launch failed; see attn_status_string */
+} attn_status;
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+/*
+ * Masks.  Query row i of a sequence stands at key position pos = i + (Nk - Nq)
+ * (bottom-right alignment, so a single decoding query sees its whole cache).
+ *   NONE            every key is visible.
+ *   CAUSAL          key j is visible iff j <= pos ("Attention and matrix
+ *                   kernels" page, How it works: causal masks).
+ *   SLIDING_WINDOW  key j is visible iff 0 <= pos - j < window, i.e. the
+ *                   `window` latest positions including the query's own
+ *                   ("Attention Is the Bottleneck", Sliding windows and
+ *                   local:global layers).  window >= 1.
+ *   DOCUMENT        causal inside packed documents: key j is visible iff
+ *                   j <= pos and j lies in the same document as pos
+ *                   ("Attention and matrix kernels", document masks).
+ *                   doc_offsets is a DEVICE int32 array of num_docs + 1
+ *                   strictly increasing entries, doc_offsets[0] = 0 and
+ *                   doc_offsets[num_docs] = Nk; document t holds key
+ *                   positions [doc_offsets[t], doc_offsets[t+1]).  The same
+ *                   offsets apply to every batch element.
+ * A query row that sees no key gets O = 0 and LSE = -inf.
+ */
+typedef enum {
+    ATTN_MASK_NONE = 0,
+    ATTN_MASK_CAUSAL = 1,
+    ATTN_MASK_SLIDING_WINDOW = 2,
+    ATTN_MASK_DOCUMENT = 3
+} attn_mask_kind;
+
+typedef struct {
+    int32_t kind;               /* an attn_mask_kind */
+    int32_t window;             /* SLIDING_WINDOW only: W >= 1 */
+    const int32_t* doc_offsets; /* DOCUMENT only: device pointer, num_docs + 1 entries */
+    int32_t num_docs;           /* DOCUMENT only: >= 1 */
+} attn_mask;
+
+/*
+ * attn_fwd — attention forward for a batch of prompts (prefill).
+ *
+ *   q    [B, Hq,  Nq, d]  dtype          read only
+ *   k    [B, Hkv, Nk, d]  dtype          read only
+ *   v    [B, Hkv, Nk, d]  dtype          read only
+ *   o    [B, Hq,  Nq, d]  dtype          written in full
+ *   lse  [B, Hq,  Nq]     float32        natural-log log-sum-exp of each row's
+ *                                        scaled visible scores (the saved
+ *                                        softmax statistic the "Attention Is
+ *                                        the Bottleneck" page names for the
+ *                                        backward pass); may be NULL.
+ *
+ * Grouped-query heads (MQA and GQA section of the same page): Hq must be a
+ * multiple of Hkv and query head h reads KV head h / (Hq / Hkv).
+ * `scale` multiplies Q K^T before the mask; pass 1/sqrt(d) for the usual
+ * attention.  d must be 64 or 128.  Sizes of 0 are accepted and enqueue
+ * nothing.  bf16 inputs produce a bf16 output rounded to nearest-even; the
+ * softmax statistics and accumulators are float32 in both dtypes.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             attn_mask mask, int dtype, hipStream_t stream);
+
+/*
+ * attn_paged_decode_workspace_size — bytes of scratch device memory that
+ * attn_paged_decode needs for these sizes (the per-split partial outputs and
+ * log-sum-exps that its combine pass merges).  Returns 0 for invalid sizes.
+ */
+size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, int max_seq_len);
+
+/*
+ * attn_paged_decode — one new token per sequence attends to that sequence's
+ * paged KV cache (paged-attention kernels, "Attention and matrix kernels"
+ * page; Paging and prefix sharing, "Attention Is the Bottleneck").  The KV
+ * sequence of each (sequence, KV head) is split into chunks that are
+ * attended in parallel and then merged with a log-sum-exp combine
+ * (Flash-Decoding section of the same page).
+ *
+ *   q            [num_seqs, Hq, d]                       bf16, read only
+ *   k_pages      [num_pages, Hkv, page_size, d]          bf16, read only
+ *   v_pages      [num_pages, Hkv, page_size, d]          bf16, read only
+ *   block_table  [num_seqs, max_pages_per_seq]           int32; entry p of a
+ *                sequence is the physical page holding its tokens
+ *                [p*page_size, (p+1)*page_size)
+ *   seq_lens     [num_seqs]                              int32, 0 <= len <= max_seq_len
+ *   o            [num_seqs, Hq, d]                       bf16, written in full
+ *   lse          [num_seqs, Hq]                          float32 natural-log LSE; may be NULL
+ *   workspace    device scratch of at least
+ *                attn_paged_decode_workspace_size(num_seqs, Hq, d, max_seq_len)
+ *                bytes, 16-byte aligned; its contents on entry do not matter.
+ *
+ * The query is the newest token, so it sees all seq_len cached keys.  Page
+ * slots past seq_len are never read into the result (they may hold any bit
+ * pattern, NaN included).  A sequence with seq_len = 0 gets O = 0 and
+ * LSE = -inf.  page_size must be 16, d must be 128 or 64, Hq a multiple of
+ * Hkv, max_pages_per_seq * page_size >= max_seq_len.  The workspace must not
+ * be shared by calls that may run concurrently.
+ */
+int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      void* o, float* lse,
+                      int num_seqs, int Hq, int Hkv, int d, int page_size,
+                      int max_pages_per_seq, int max_seq_len, float scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text for a status code (static storage; for ATTN_ERR_HIP, thread-local). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -1,0 +1,93 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_fwd_amd as xa
+from exact_io_aware_fwd_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "exact_attn.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
+                                    "attn_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert xa.status_string(0) == "ok"
+    assert "invalid" in xa.status_string(1)
+    assert "unsupported" in xa.status_string(2)
+    assert "workspace" in xa.status_string(3)
+    assert xa.status_string(99) == "unknown status"
+
+
+def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.1,
+        kind=0, window=0, doc=None, num_docs=0, dtype=1):
+    m = _lib.AttnMask(kind, window, doc, num_docs)
+    return _lib.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 2), (dict(d=256), 2), (dict(d=-1), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(Hkv=0), 1), (dict(B=-1), 1), (dict(Nq=-3), 1),
+    (dict(dtype=7), 1), (dict(kind=9), 1),
+    (dict(kind=2, window=0), 1), (dict(kind=3, num_docs=0, doc=FAKE), 1), (dict(kind=3, num_docs=2, doc=None), 1),
+    (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(k=None), 1), (dict(q=FAKE + 4), 1), (dict(v=FAKE + 8), 1),
+    (dict(Nq=1 << 29), 2),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_fwd_empty_problems_are_noops():
+    # nothing is enqueued, so null pointers are fine
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, Nq=0) == 0
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, Hq=0, Hkv=0) == 0
+
+
+def dec(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128, page=16,
+        max_pages=4, max_len=64, scale=0.1, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = xa.attn_paged_decode_workspace_size(S, Hq, d, max_len)
+    return _lib.lib().attn_paged_decode(q, kp, vp, bt, sl, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
+                                        scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=32), 2), (dict(d=96), 2), (dict(Hq=6, Hkv=4), 1), (dict(max_pages=3), 1),
+    (dict(S=-1), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(sl=None), 1), (dict(bt=None), 1),
+    (dict(kp=FAKE + 2), 1), (dict(ws_bytes=16), 3), (dict(ws=None), 3),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_empty_is_noop():
+    assert dec(q=None, o=None, S=0) == 0
+
+
+def test_workspace_size():
+    f = xa.attn_paged_decode_workspace_size
+    assert f(64, 32, 128, 32768) >= 64 * 32 * 64 * 129 * 4
+    assert f(64, 32, 128, 32768) < 64 * 32 * 64 * 129 * 4 + 4096
+    assert f(64, 32, 128, 1024) < f(64, 32, 128, 1025) <= f(64, 32, 128, 2048)
+    assert f(1, 1, 96, 10) == 0 and f(-1, 1, 128, 10) == 0

@@ -1,0 +1,41 @@
+"""Host-side work accounting of the benchmark, checked against the oracle's
+mask and against the decode byte arithmetic on the attention pages."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+@pytest.mark.parametrize("Nq,Nk,mask,window,offs", [
+    (37, 37, "none", 0, None), (37, 37, "causal", 0, None), (20, 50, "causal", 0, None), (50, 20, "causal", 0, None),
+    (64, 64, "window", 5, None), (30, 60, "window", 17, None), (40, 40, "document", 0, [0, 3, 4, 20, 40]),
+])
+def test_visible_pairs_matches_oracle_mask(Nq, Nk, mask, window, offs):
+    assert bench.visible_pairs(Nq, Nk, mask, window, offs) == int(oracle.visibility(Nq, Nk, mask, window, offs).sum())
+
+
+def test_config_pair_counts():
+    assert bench.visible_pairs(2048, 2048, "causal") == 2_098_176
+    assert bench.visible_pairs(8192, 8192, "causal") == 33_558_528
+    assert bench.visible_pairs(8192, 8192, "window", 1024) == 7_864_832
+    c = workloads.make_prefill(1, 1, 1, 32768, 32768, 8, mask="document", doc_min=512, doc_max=8192, seed=0)
+    assert bench.visible_pairs(32768, 32768, "document", 0, c["doc_offsets"]) == 77_679_895
+
+
+def test_decode_bytes_match_the_pages_arithmetic():
+    # "Attention Is the Bottleneck", Prefill and decode: a Llama-3-8B-shaped KV
+    # cache (8 KV heads, head dim 128, bf16) holds 2*8*128*2 = 4096 bytes per
+    # token per layer; x 32 layers = 131,072 bytes = 128 KiB per token.
+    c = dict(seq_lens=np.array([32768]), num_seqs=1, Hq=32, Hkv=8, d=128, page_size=16)
+    kv = bench.decode_bytes(c) - (2 * 32 * 128 * 2 + 32 * 4 + 2048 * 4 + 4)
+    assert kv == 32768 * 4096
+    assert kv * 32 == 4 * 2**30              # 4 GiB per generated token at 32K context, all 32 layers
+    assert kv * 32 / 3.35e12 == pytest.approx(1.28e-3, rel=0.01)   # ~1.3 ms at 3.35 TB/s
+
+
+def test_decode_config_bytes():
+    c = workloads.decode_config("c5_paged_decode_64", with_values=False)
+    assert int(c["seq_lens"].sum()) == 1_101_299
+    assert bench.decode_bytes(c) == 4_512_253_168

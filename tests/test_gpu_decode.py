@@ -1,0 +1,88 @@
+"""Paged split-K decode parity on the GPU against the fp64 oracle, plus the
+invariances the method must keep (page placement, workspace contents, runs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from exact_io_aware_fwd_amd import attn_paged_decode, attn_paged_decode_workspace_size
+from _gpu_helpers import BF16_TOL, compare, dev, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(c):
+    return dict(q=dev(c["q"], "bf16"), k=dev(c["k_pages"], "bf16"), v=dev(c["v_pages"], "bf16"),
+                bt=torch.from_numpy(c["block_table"]).cuda(), sl=torch.from_numpy(c["seq_lens"]).cuda())
+
+
+def run(c, t=None, workspace=None):
+    t = t or to_dev(c)
+    o, lse = attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], max_seq_len=c["max_seq_len"],
+                               scale=c["scale"], workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(c, label, seqs=None):
+    say(f"[case] {label} S={c['num_seqs']} Hq={c['Hq']} Hkv={c['Hkv']} d={c['d']} lens={c['seq_lens'][:8].tolist()}")
+    o, lse = run(c)
+    og, lg = host_f64(o), host_f64(lse)
+    o_ref, l_ref = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                       c["scale"], seqs=seqs, dtype="bf16")
+    if seqs is not None:
+        og, lg = og[list(seqs)], lg[list(seqs)]
+    return compare(og, lg, o_ref, l_ref, BF16_TOL, label)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 1), (32, 2), (6, 2), (2, 2)])
+def test_decode_small(d, Hq, Hkv):
+    lens = [0, 1, 15, 16, 17, 511, 512, 513, 1500, 1024]
+    c = workloads.make_decode(len(lens), Hq, Hkv, d, seq_lens=lens, max_seq_len=1600, seed=21,
+                              tail_fill="nan", extra_pages=5)
+    check(c, f"decode d{d} Hq{Hq} Hkv{Hkv}")
+
+
+def test_decode_random_lengths_nan_tails():
+    c = workloads.make_decode(24, 32, 8, 128, len_min=1, len_max=5000, seed=23, tail_fill="nan")
+    check(c, "decode random lens")
+
+
+def test_decode_page_permutation_invariance():
+    c = workloads.make_decode(6, 8, 2, 128, len_min=100, len_max=3000, seed=25, extra_pages=4)
+    o1, l1 = run(c)
+    pi = np.random.default_rng(26).permutation(c["k_pages"].shape[0])
+    c2 = dict(c)
+    for key in ("k_pages", "v_pages"):
+        arr = np.empty_like(c[key])
+        arr[pi] = c[key]
+        c2[key] = arr
+    bt = c["block_table"].copy()
+    valid = bt >= 0
+    bt[valid] = pi[bt[valid]]
+    c2["block_table"] = bt
+    o2, l2 = run(c2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_workspace_contents_and_determinism():
+    c = workloads.make_decode(5, 8, 2, 128, len_min=10, len_max=2000, seed=27)
+    t = to_dev(c)
+    need = attn_paged_decode_workspace_size(5, 8, 128, c["max_seq_len"])
+    ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    o1, l1 = run(c, t, workspace=ws.view(torch.uint8)[:need])
+    o2, l2 = run(c, t)
+    o3, l3 = run(c, t)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
+
+
+@pytest.mark.slow
+def test_config_paged_decode_64():
+    c = workloads.decode_config("c5_paged_decode_64")
+    lens = c["seq_lens"]
+    seqs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
+                      np.random.default_rng(3).choice(64, 14, replace=False).tolist()))
+    check(c, f"c5 sampled {len(seqs)} of 64 sequences", seqs=seqs)

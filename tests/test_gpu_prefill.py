@@ -1,0 +1,147 @@
+"""Prefill parity on the GPU: the HIP kernels against the fp64 oracle.
+
+Tolerances: fp32 max-abs 1e-5 on O; bf16 max-abs 1e-2 and mean-abs 1e-3 on
+O; LSE max-abs 1e-3; rows that see no key exactly O = 0, LSE = -inf.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from exact_io_aware_fwd_amd import attn_fwd
+from _gpu_helpers import BF16_TOL, F32_TOL, compare, dev, doc_tensor, host_f64, oracle_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(case, rows=None, label=""):
+    dt = case["dtype"]
+    say(f"[case] {label} B={case['B']} Hq={case['Hq']} Hkv={case['Hkv']} Nq={case['Nq']} Nk={case['Nk']} "
+        f"d={case['d']} {dt} mask={case['mask']} W={case['window']}")
+    q, k, v = dev(case["q"], dt), dev(case["k"], dt), dev(case["v"], dt)
+    o, lse = attn_fwd(q, k, v, scale=case["scale"], mask=case["mask"], window=case["window"],
+                      doc_offsets=doc_tensor(case))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_prefill(case, rows=rows)
+    og, lg = host_f64(o), host_f64(lse)
+    if rows is not None:
+        og, lg = og[:, :, rows], lg[:, :, rows]
+    return compare(og, lg, o_ref, lse_ref, F32_TOL if dt == "f32" else BF16_TOL, label)
+
+
+def test_single_head_f32_config():
+    case = workloads.prefill_config("c1_f32_single_head")
+    run_case(case, label="c1")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 37)])
+def test_f32_small(d, mask, window):
+    case = workloads.make_prefill(2, 4, 2, 200, 200, d, dtype="f32", seed=11, mask=mask, window=window)
+    run_case(case, label=f"f32 d{d} {mask}")
+
+
+SHAPES = [1, 31, 64, 65, 128, 129, 300, 1000]
+
+
+@pytest.mark.parametrize("N", SHAPES)
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_bf16_ragged_lengths(N, mask):
+    case = workloads.make_prefill(2, 4, 2, N, N, 128, seed=N, mask=mask)
+    run_case(case, label=f"bf16 N{N} {mask}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 1), ("window", 7),
+                                         ("window", 200), ("window", 5000)])
+def test_bf16_masks(d, mask, window):
+    case = workloads.make_prefill(1, 8, 2, 777, 777, d, seed=3, mask=mask, window=window)
+    run_case(case, label=f"bf16 d{d} {mask} W{window}")
+
+
+@pytest.mark.parametrize("lens", [[100, 1, 50, 149], [300], [64, 64, 64, 64, 10], [1] * 20 + [280]])
+def test_bf16_document(lens):
+    N = sum(lens)
+    case = workloads.make_prefill(2, 4, 1, N, N, 128, seed=5, mask="document", doc_lens=lens)
+    run_case(case, label=f"bf16 doc {lens[:5]}")
+
+
+@pytest.mark.parametrize("Nq,Nk,mask", [(100, 300, "causal"), (300, 100, "causal"), (1, 500, "causal"),
+                                        (50, 400, "window"), (200, 77, "none"), (129, 1, "none")])
+def test_bf16_unequal_lengths(Nq, Nk, mask):
+    case = workloads.make_prefill(1, 4, 4, Nq, Nk, 128, seed=7, mask=mask, window=60)
+    run_case(case, label=f"bf16 Nq{Nq} Nk{Nk} {mask}")
+
+
+def test_bf16_mqa():
+    case = workloads.make_prefill(1, 8, 1, 333, 333, 128, seed=9, mask="causal")
+    run_case(case, label="bf16 mqa")
+
+
+def test_outputs_written_in_place_only():
+    """Guard bands around o and lse stay untouched, q/k/v stay unchanged."""
+    case = workloads.make_prefill(1, 4, 2, 130, 130, 128, seed=13, mask="causal")
+    q, k, v = dev(case["q"], "bf16"), dev(case["k"], "bf16"), dev(case["v"], "bf16")
+    q0, k0, v0 = q.clone(), k.clone(), v.clone()
+    n = q.numel()
+    obuf = torch.full((n + 2048,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((4 * 130 + 128,), float("nan"), dtype=torch.float32, device="cuda")
+    o = obuf[1024:1024 + n].view(q.shape)
+    lse = lbuf[64:64 + 4 * 130].view(1, 4, 130)
+    attn_fwd(q, k, v, mask="causal", out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[:1024]).all() and torch.isnan(obuf[1024 + n:]).all()
+    assert torch.isnan(lbuf[:64]).all() and torch.isnan(lbuf[64 + 4 * 130:]).all()
+    assert torch.equal(q, q0) and torch.equal(k, k0) and torch.equal(v, v0)
+    assert torch.isfinite(o.float()).all()
+
+
+def test_deterministic_run_to_run():
+    case = workloads.make_prefill(2, 8, 2, 1000, 1000, 128, seed=17, mask="causal")
+    q, k, v = dev(case["q"], "bf16"), dev(case["k"], "bf16"), dev(case["v"], "bf16")
+    o1, l1 = attn_fwd(q, k, v, mask="causal")
+    o2, l2 = attn_fwd(q, k, v, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_optional():
+    case = workloads.make_prefill(1, 2, 2, 100, 100, 64, seed=19, mask="causal")
+    q, k, v = dev(case["q"], "bf16"), dev(case["k"], "bf16"), dev(case["v"], "bf16")
+    o1, _ = attn_fwd(q, k, v, mask="causal", with_lse=False)
+    o2, _ = attn_fwd(q, k, v, mask="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------ full-size configs
+
+def sample_rows(N, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    base = {0, 1, 127, 128, N - 1, N - 2, N // 2}
+    base.update(int(x) for x in extra if 0 <= x < N)
+    base.update(rng.choice(N, size=min(N, 384), replace=False).tolist())
+    return np.array(sorted(base))
+
+
+@pytest.mark.slow
+def test_config_causal_b4h16n2048_all_rows():
+    case = workloads.prefill_config("c2_causal_b4h16n2048")
+    run_case(case, label="c2 all rows")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["c3a_gqa_causal_n8192", "c3b_gqa_window1024_n8192"])
+def test_config_gqa_n8192_sampled_rows(name):
+    case = workloads.prefill_config(name)
+    rows = sample_rows(case["Nq"], 1, extra=range(1020, 1030))
+    run_case(case, rows=rows, label=f"{name} sampled {rows.size} rows/head")
+
+
+@pytest.mark.slow
+def test_config_document_n32768_sampled_rows():
+    case = workloads.prefill_config("c4_document_n32768")
+    off = case["doc_offsets"]
+    edges = list(off[:-1]) + list(off[1:] - 1) + list(off[1:-1] - 1) + list(off[1:-1] + 1)
+    rows = sample_rows(case["Nq"], 2, extra=edges)
+    run_case(case, rows=rows, label=f"c4 sampled {rows.size} rows/head")

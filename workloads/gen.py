@@ -1,8 +1,11 @@
 """Seeded generators for the attention workloads.
 
-Every array is drawn from ``numpy.random.default_rng(seed)`` in a fixed order:
-structure first (document lengths, context lengths, page permutation), then
-Q, K and V, each as float32 standard normals.  bf16 workloads are rounded to
+The structure (document lengths, context lengths, page permutation) is drawn
+from ``numpy.random.default_rng(seed)``.  Q, K and V are then float32
+standard normals, each tensor from its own stream: draw number n (Q = 1,
+K = 2, V = 3) of a problem with seed s is cut into chunks of 2**24 values and
+chunk i comes from ``default_rng(SeedSequence([s, n]).spawn(...)[i])``, so
+large tensors can be drawn on several threads with a fixed result.  bf16 workloads are rounded to
 bf16 with round-to-nearest-even and handed out as raw ``uint16`` bit patterns,
 so the GPU side can view them as bf16 without another rounding and the
 oracle side can widen them exactly.
@@ -15,7 +18,9 @@ Shapes follow the layouts of the C ABI:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 
 import numpy as np
 
@@ -60,13 +65,33 @@ def bf16_bits_from_f32(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
     return out.reshape(x.shape)
 
 
-def _draw(rng: np.random.Generator, shape, dtype: str):
-    x = rng.standard_normal(shape, dtype=np.float32)
-    if dtype == "f32":
-        return x
-    if dtype == "bf16":
-        return bf16_bits_from_f32(x)
-    raise ValueError(f"unknown dtype {dtype}")
+CHUNK = 1 << 24
+
+
+def _draw(seed: int, stream: int, shape, dtype: str):
+    """Standard normals for one tensor (see the module docstring for the stream)."""
+    n = int(np.prod(shape))
+    nchunks = max(1, -(-n // CHUNK))
+    kids = np.random.SeedSequence([seed, stream]).spawn(nchunks)
+    x = np.empty(n, dtype=np.float32)
+    out = np.empty(n, dtype=np.uint16) if dtype == "bf16" else x
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype}")
+
+    def fill(i):
+        sl = slice(i * CHUNK, min(n, (i + 1) * CHUNK))
+        np.random.default_rng(kids[i]).standard_normal(sl.stop - sl.start, dtype=np.float32, out=x[sl])
+        if dtype == "bf16":
+            out[sl] = bf16_bits_from_f32(x[sl])
+
+    workers = min(16, len(os.sched_getaffinity(0)), nchunks)
+    if workers <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
 
 
 def doc_lengths(rng: np.random.Generator, total: int, lo: int, hi: int) -> list[int]:
@@ -102,9 +127,9 @@ def make_prefill(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, *, dtype: 
             doc_lens = doc_lengths(rng, Nk, doc_min, doc_max)
         assert sum(doc_lens) == Nk
         offsets = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32)
-    q = _draw(rng, (B, Hq, Nq, d), dtype)
-    k = _draw(rng, (B, Hkv, Nk, d), dtype)
-    v = _draw(rng, (B, Hkv, Nk, d), dtype)
+    q = _draw(seed, 1, (B, Hq, Nq, d), dtype)
+    k = _draw(seed, 2, (B, Hkv, Nk, d), dtype)
+    v = _draw(seed, 3, (B, Hkv, Nk, d), dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return dict(kind="prefill", q=q, k=k, v=v, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk,
@@ -116,15 +141,17 @@ def make_decode(num_seqs: int, Hq: int, Hkv: int, d: int, *, page_size: int = 16
                 len_min: int = 1024, len_max: int = 32768, seed: int = 0,
                 seq_lens: list[int] | None = None, max_seq_len: int | None = None,
                 tail_fill: str = "zero", extra_pages: int = 0,
-                scale: float | None = None) -> dict:
+                scale: float | None = None, with_values: bool = True) -> dict:
     """Draw one paged-decode problem (bf16 only).
 
     Context lengths are uniform in [len_min, len_max] unless given.  Every
     sequence's logical pages are laid out in order and then sent to physical
-    pages by one seeded permutation of all pages.  Page slots past a
+    pages by one seeded permutation of all pages.  K and V values are drawn
+    for all slots in physical page order.  Page slots past a
     sequence's length hold zeros (``tail_fill="zero"``) or quiet NaNs
     (``"nan"``); ``extra_pages`` adds that many unreferenced pages filled the
-    same way.
+    same way.  ``with_values=False`` stops after the structure (lengths,
+    block table) and the query, leaving the page arrays as None.
     """
     rng = np.random.default_rng(seed)
     if seq_lens is None:
@@ -145,28 +172,23 @@ def make_decode(num_seqs: int, Hq: int, Hkv: int, d: int, *, page_size: int = 16
         block_table[s, :npg] = perm[g:g + npg]
         g += npg
 
-    q = _draw(rng, (num_seqs, Hq, d), "bf16")
-    total_tokens = int(sum(seq_lens))
-    # physical (page, slot) of every valid token, sequence by sequence
-    tok_page = np.empty(total_tokens, dtype=np.int64)
-    tok_slot = np.empty(total_tokens, dtype=np.int64)
-    t0 = 0
-    for s, n in enumerate(seq_lens):
-        t = np.arange(n)
-        tok_page[t0:t0 + n] = block_table[s, t // page_size]
-        tok_slot[t0:t0 + n] = t % page_size
-        t0 += n
-
+    q = _draw(seed, 1, (num_seqs, Hq, d), "bf16")
     fill = np.uint16(0) if tail_fill == "zero" else BF16_QNAN
     pages = []
-    for _ in range(2):  # K then V
-        vals = _draw(rng, (total_tokens, Hkv, d), "bf16")
-        arr = np.full((num_pages, Hkv, page_size, d), fill, dtype=np.uint16)
-        arr[tok_page, :, tok_slot, :] = vals
-        del vals
+    for stream in ((2, 3) if with_values else ()):  # K then V
+        # every slot of every page is drawn in physical page order; slots past
+        # a sequence's end (and unreferenced pages) are then overwritten
+        arr = _draw(seed, stream, (num_pages, Hkv, page_size, d), "bf16")
+        for s, n in enumerate(seq_lens):
+            if n % page_size:
+                arr[block_table[s, n // page_size], :, n % page_size:, :] = fill
+        if extra_pages:
+            arr[perm[used_pages:]] = fill
         pages.append(arr)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if not with_values:
+        pages = [None, None]
     return dict(kind="decode", q=q, k_pages=pages[0], v_pages=pages[1], block_table=block_table,
                 seq_lens=np.asarray(seq_lens, dtype=np.int32), num_seqs=num_seqs, Hq=Hq, Hkv=Hkv,
                 d=d, page_size=page_size, max_seq_len=int(max_seq_len), scale=float(np.float32(scale)),
