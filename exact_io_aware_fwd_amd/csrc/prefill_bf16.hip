@@ -26,33 +26,185 @@ namespace xattn {
 
 template <int D>
 struct PrefillBf16Cfg {
-    static constexpr int BM = 128;          // query rows per workgroup
-    static constexpr int BN = 64;           // keys per K/V tile
-    static constexpr int KSTR = D + 8;      // bf16 per K row in LDS (16 B pad: rows shift banks)
-    static constexpr int VSTR = BN + 8;     // bf16 per V^T row in LDS
-    static constexpr int DK = D / 16;       // MFMA steps over the head dim for S
-    static constexpr int CB = D / 32;       // 32-wide blocks of the head dim for O
-    static constexpr int K_CHUNKS = BN * D / 8 / 256;            // 16-byte K loads per thread
-    static constexpr int V_GROUPS = (BN / 4) * (D / 8);          // 4 keys x 8 columns each
-    static constexpr int V_PER_THREAD = (V_GROUPS + 255) / 256;
+    static constexpr int BM = 128;               // query rows per workgroup (4 waves x 32)
+    static constexpr int BN = 64;                // keys per K/V tile
+    static constexpr int CHUNKS = D / 8;         // 16-byte chunks per K/V row
+    // Row strides in LDS, in 16-byte slots.  One slot of padding per K row
+    // puts 16 consecutive rows on 16 different 16-byte bank groups (the K
+    // operand reads one chunk of 16 consecutive rows); two slots per V row put
+    // 4 consecutive rows x 32 bytes on distinct banks (the transposed V reads).
+    static constexpr int KS = CHUNKS + 1;
+    static constexpr int VS = CHUNKS + 2;
+    static constexpr int KTILE = BN * KS * 16;   // bytes per K tile in LDS
+    static constexpr int VTILE = BN * VS * 16;
+    static constexpr int KLOADS = KTILE / 1024;  // 1 KiB direct loads per K tile
+    static constexpr int VLOADS = VTILE / 1024;
+    static constexpr int KLW = (KLOADS + 3) / 4; // per wave (rounded up)
+    static constexpr int VLW = (VLOADS + 3) / 4;
+    static constexpr int DK = D / 16;            // MFMA steps over the head dim for S
+    static constexpr int CB = D / 32;            // 32-wide blocks of the head dim for O
+    static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "tiles must be whole 1 KiB blocks");
 };
 
-// Position of 4-key group `kg` (keys 4kg..4kg+3 of the tile) inside the V^T
-// rows: within each 16-key block the two middle groups trade places, matching
-// the key order of the P^T operand built from the S^T accumulator.
-__device__ __forceinline__ int vt_pos(int kg) {
-    const int sub = kg & 3;
-    const int psub = (sub == 1) ? 2 : (sub == 2 ? 1 : sub);
-    return (kg >> 2) * 16 + psub * 4;
+// Softmax weights are kept relative to a stale row max until a tile's max
+// exceeds it by more than 2^8; only then is the accumulator rescaled (the
+// conditional rescaling of FlashAttention-4, "Attention Is the Bottleneck").
+// Weights stay below 256, well inside fp32 and bf16 range, and the result is
+// unchanged because O and the row sums share the same reference.
+constexpr float kRescaleThreshold = 8.f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane byte offsets into one K or V tile in global memory for this wave's
+// direct loads.  Load i of the tile fills LDS bytes [1024 i, 1024 i + 1024):
+// lane l lands on 16-byte slot 64 i + l, i.e. row (64 i + l) / S, chunk
+// (64 i + l) % S of the padded layout.  Padding slots fetch the row's last
+// chunk again (never read back).
+template <int D, int S, int NL>
+__device__ __forceinline__ void tile_src_offsets(uint32_t (&off)[(NL + 3) / 4], int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < (NL + 3) / 4; ++j) {
+        const int slot = (wave + 4 * j) * 64 + lane;
+        const int r = slot / S;
+        int c = slot % S;
+        c = c < D / 8 ? c : D / 8 - 1;
+        off[j] = (uint32_t)((r * D + c * 8) * 2);
+    }
+}
+
+// Issue this wave's share of the direct HBM -> LDS copies of one tile
+// (buffer_load_dwordx4 ... lds).  The buffer resource starts at key n0 and
+// covers only the keys that exist, so rows past Nk read as zeros.
+template <int D, int S, int NL>
+__device__ __forceinline__ void load_tile_async(const uint16_t* __restrict__ base, int n0, int Nk, uint8_t* lds,
+                                                const uint32_t (&off)[(NL + 3) / 4], int wave) {
+    const int rows = Nk - n0;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (size_t)n0 * D), (short)0, rows * D * 2, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < (NL + 3) / 4; ++j) {
+        const int blk = wave + 4 * j;
+        if (NL % 4 == 0 || blk < NL)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 1024), 16, off[j], 0, 0, 0);
+    }
+}
+
+template <int D>
+struct PrefillBf16State {
+    bf16x8 qf[D / 16];
+    f32x16 acc[D / 32];
+    float m_run;
+    float l_run;   // this lane's half of the row sum of the bf16 weights: normalises O
+    float l_f32;   // same sum over the unrounded fp32 weights: gives the LSE
+};
+
+// S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
+// key tile resident in LDS.  kl / vl point at this lane's own base in the
+// K / V tile; every other operand address is a compile-time offset from it.
+template <int D>
+__device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t* kl, const uint8_t* vl, int n0,
+                                          bool full, int lo_i, int hi_i, float scale_log2, int lane) {
+    using C = PrefillBf16Cfg<D>;
+    // ---- S^T = K Q^T, two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) s[jb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const u32x4 a = *(const u32x4*)(kl + jb * 32 * C::KS * 16 + kk * 32);
+            s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), st.qf[kk], s[jb], 0, 0, 0);
+        }
+    // ---- mask, only where the tile is not fully visible to this wave
+    if (!full) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (key < lo_i || key > hi_i) s[jb][r] = neg_inf();
+            }
+    }
+    // ---- online softmax (base 2) with conditional rescaling
+    float mt = neg_inf();
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[jb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > st.m_run + kRescaleThreshold)) {
+        // A row that has still seen no key (both maxima -inf) keeps alpha = 0
+        // from the 0 reference instead of exp2(-inf - -inf) = NaN; its acc and
+        // sums are 0 anyway.
+        const float m_new = fmaxf(st.m_run, mt);
+        const float alpha = fast_exp2(st.m_run - (m_new == neg_inf() ? 0.f : m_new));
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] *= alpha;
+        st.l_run *= alpha;
+        st.l_f32 *= alpha;
+        st.m_run = m_new;
+    }
+    const float m_use = st.m_run == neg_inf() ? 0.f : st.m_run;
+    float fsum = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], scale_log2, -m_use));
+            fsum += s[jb][r];
+        }
+    // P^T operands (bf16), one per 16-key block.  O is normalised by the sum of
+    // the same bf16-rounded weights the PV product uses, so it is an exact
+    // weighted average of V rows under those weights (a dot with (1, 1) adds
+    // two packed bf16 values at once); the LSE uses the fp32 sum, free of the
+    // weights' rounding.
+    bf16x8 pf[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int jb = kb >> 1, h = (kb & 1) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] = pack_bf16x2(s[jb][h + 2 * e], s[jb][h + 2 * e + 1]);
+            psum = sum_bf16x2(w[e], psum);
+        }
+        pf[kb] = __builtin_bit_cast(bf16x8, w);
+    }
+    st.l_run += psum;
+    st.l_f32 += fsum;
+    // ---- O^T += V^T P^T.  The V^T operand comes from the row-major V tile
+    // through two transposing reads (ds_read_b64_tr_b16): in each 16-lane
+    // group, source lane 4k+q points at 4 columns c0+4q.. of key row k, and
+    // lane i receives column c0+i of those 4 rows.  Rows are picked so the 8
+    // keys a lane holds are the ones its P^T operand slots hold.
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint8_t* vp = vl + kb * 16 * C::VS * 16 + cb * 64;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+            st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kb], st.acc[cb], 0, 0, 0);
+        }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     using C = PrefillBf16Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::BN * C::KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * C::VSTR];
+    // two stages of the K/V ring, as separate arrays so each access names its buffer
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[C::VTILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, lets loads use scalar control
     const int nbk = p.B * p.Hkv;
     int bk, qt, g;
     decode_work(blockIdx.x, nbk, p.num_q_tiles, p.group, bk, qt, g);
@@ -79,165 +231,62 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     row_interval(p, w_last, lo_w_last, hi_w_last);
     const bool wave_has_rows = w0 < p.Nq;
 
+    PrefillBf16State<D> st;
     // Q fragment: MFMA B operand, column = query row (lane & 31), k slots
     // (lane >> 5) * 8 .. +8 of every 16-wide step of the head dim.
-    bf16x8 qf[C::DK];
     {
         const uint16_t* qrow = qg + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + (row_ok ? row : 0)) * D;
 #pragma unroll
         for (int kk = 0; kk < C::DK; ++kk) {
             u32x4 w = row_ok ? *(const u32x4*)(qrow + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            st.qf[kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-
-    f32x16 acc[C::CB];
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
-    float m_run = neg_inf();   // running row max, base-2 scaled units
-    float l_run = 0.f;         // this lane's half of the running row sum
+    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
+    st.m_run = neg_inf();   // running row max, base-2 scaled units
+    st.l_run = 0.f;
+    st.l_f32 = 0.f;
 
     const int t_begin = lo_wg / C::BN;
     const int t_end = hi_wg >= lo_wg ? hi_wg / C::BN : t_begin - 1;
 
-    // Register staging for the next K/V tile.
-    u32x4 kreg[C::K_CHUNKS];
-    u32x4 vreg[C::V_PER_THREAD][4];
+    uint32_t koff[C::KLW], voff[C::VLW];
+    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
+    // this lane's operand bases inside a K / V tile
+    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
 
-    auto load_tile = [&](int t) {
+    // One stage of the ring: wait for this tile's copies, make them visible to
+    // every wave (which also proves every wave is done with the other stage),
+    // start copying the next tile into the other stage, then compute.
+    auto stage = [&](int t, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
+        __syncthreads();
+        if (t < t_end) {
+            load_tile_async<D, C::KS, C::KLOADS>(kg_, (t + 1) * C::BN, p.Nk, kn, koff, wave);
+            load_tile_async<D, C::VS, C::VLOADS>(vg_, (t + 1) * C::BN, p.Nk, vn, voff, wave);
+        }
         const int n0 = t * C::BN;
-#pragma unroll
-        for (int u = 0; u < C::K_CHUNKS; ++u) {
-            const int c = u * 256 + tid;
-            const int r = c / (D / 8), c8 = c % (D / 8);
-            const int key = n0 + r;
-            kreg[u] = key < p.Nk ? *(const u32x4*)(kg_ + (size_t)key * D + c8 * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int s = 0; s < C::V_PER_THREAD; ++s) {
-            const int gidx = s * 256 + tid;
-            const int cc = gidx % (D / 8), kgp = gidx / (D / 8);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int key = n0 + kgp * 4 + u;
-                vreg[s][u] = (gidx < C::V_GROUPS && key < p.Nk)
-                                 ? *(const u32x4*)(vg_ + (size_t)key * D + cc * 8)
-                                 : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < C::K_CHUNKS; ++u) {
-            const int c = u * 256 + tid;
-            const int r = c / (D / 8), c8 = c % (D / 8);
-            *(u32x4*)(&k_lds[buf][r * C::KSTR + c8 * 8]) = kreg[u];
-        }
-#pragma unroll
-        for (int s = 0; s < C::V_PER_THREAD; ++s) {
-            const int gidx = s * 256 + tid;
-            if (gidx < C::V_GROUPS) {
-                const int cc = gidx % (D / 8), kgp = gidx / (D / 8);
-                const int pos = vt_pos(kgp);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    // columns 8cc+2w (low halves) and 8cc+2w+1 (high halves)
-                    const uint32_t lo01 = __builtin_amdgcn_perm(vreg[s][1][w], vreg[s][0][w], 0x05040100u);
-                    const uint32_t lo23 = __builtin_amdgcn_perm(vreg[s][3][w], vreg[s][2][w], 0x05040100u);
-                    const uint32_t hi01 = __builtin_amdgcn_perm(vreg[s][1][w], vreg[s][0][w], 0x07060302u);
-                    const uint32_t hi23 = __builtin_amdgcn_perm(vreg[s][3][w], vreg[s][2][w], 0x07060302u);
-                    *(u32x2*)(&vt_lds[buf][(cc * 8 + 2 * w) * C::VSTR + pos]) = u32x2{lo01, lo23};
-                    *(u32x2*)(&vt_lds[buf][(cc * 8 + 2 * w + 1) * C::VSTR + pos]) = u32x2{hi01, hi23};
-                }
-            }
+        const bool active = wave_has_rows && n0 <= hi_w_last && n0 + C::BN - 1 >= lo_w_first;
+        if (active) {
+            const bool full = n0 >= lo_w_last && n0 + C::BN - 1 <= hi_w_first;
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, p.scale_log2, lane);
         }
     };
 
     if (t_begin <= t_end) {
-        load_tile(t_begin);
-        store_tile(0);
-        __syncthreads();
-        for (int t = t_begin; t <= t_end; ++t) {
-            const int buf = (t - t_begin) & 1;
-            const bool has_next = t < t_end;
-            if (has_next) load_tile(t + 1);
-            const int n0 = t * C::BN;
-            const bool active = wave_has_rows && n0 <= hi_w_last && n0 + C::BN - 1 >= lo_w_first;
-            if (active) {
-                const uint16_t* kl = k_lds[buf];
-                const uint16_t* vl = vt_lds[buf];
-                // ---- S^T = K Q^T, two 32-key blocks
-                f32x16 s[2];
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    s[jb] = f32x16{};
-#pragma unroll
-                    for (int kk = 0; kk < C::DK; ++kk) {
-                        const u32x4 a = *(const u32x4*)(kl + (jb * 32 + (lane & 31)) * C::KSTR + kk * 16 + (lane >> 5) * 8);
-                        s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], s[jb], 0, 0, 0);
-                    }
-                }
-                // ---- mask, only where the tile is not fully visible to this wave
-                const bool full = n0 >= lo_w_last && n0 + C::BN - 1 <= hi_w_first;
-                if (!full) {
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                            if (key < lo_i || key > hi_i) s[jb][r] = neg_inf();
-                        }
-                }
-                // ---- online softmax
-                float mt = neg_inf();
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[jb][r]);
-                mt = fmaxf(mt, __shfl_xor(mt, 32));
-                const float m_new = fmaxf(m_run, mt * p.scale_log2);
-                const float m_use = m_new == neg_inf() ? 0.f : m_new;
-                const float alpha = fast_exp2(m_run - m_use);
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], p.scale_log2, -m_use));
-                // ---- P^T operands (bf16), one per 16-key block.  The row sum is
-                // taken over the same bf16-rounded weights the PV product uses, so
-                // the output is an exact weighted average of V rows under those
-                // weights (a dot with (1, 1) adds two packed bf16 values at once).
-                bf16x8 pf[4];
-                float psum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const int jb = kb >> 1, h = (kb & 1) * 8;
-                    u32x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        w[e] = pack_bf16x2(s[jb][h + 2 * e], s[jb][h + 2 * e + 1]);
-                        psum = sum_bf16x2(w[e], psum);
-                    }
-                    pf[kb] = __builtin_bit_cast(bf16x8, w);
-                }
-                l_run = l_run * alpha + psum;
-                m_run = m_new;
-                if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-                    for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
-                }
-                // ---- O^T += V^T P^T
-#pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        const u32x4 a = *(const u32x4*)(vl + (cb * 32 + (lane & 31)) * C::VSTR + kb * 16 + (lane >> 5) * 8);
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kb], acc[cb], 0, 0, 0);
-                    }
-            }
-            if (has_next) store_tile(buf ^ 1);
-            __syncthreads();
+        load_tile_async<D, C::KS, C::KLOADS>(kg_, t_begin * C::BN, p.Nk, k_lds0, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(vg_, t_begin * C::BN, p.Nk, v_lds0, voff, wave);
+        for (int t = t_begin; t <= t_end; t += 2) {
+            stage(t, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (t + 1 <= t_end) stage(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     }
+    f32x16* acc = st.acc;
+    const float m_run = st.m_run, l_run = st.l_run;
+    const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
 
     // ---- epilogue: O = acc / l once, LSE in natural log
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -256,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
             }
         if (p.lse != nullptr && lane < 32) {
             p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] =
-                any ? (m_run + fast_log2(l_tot)) * kLn2 : neg_inf();
+                any ? (m_run + fast_log2(lf_tot)) * kLn2 : neg_inf();
         }
     }
 }
