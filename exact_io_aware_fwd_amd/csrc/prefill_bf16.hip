@@ -29,12 +29,14 @@ struct PrefillBf16Cfg {
     static constexpr int BM = 128;               // query rows per workgroup (4 waves x 32)
     static constexpr int BN = 64;                // keys per K/V tile
     static constexpr int CHUNKS = D / 8;         // 16-byte chunks per K/V row
-    // Row strides in LDS, in 16-byte slots.  One slot of padding per K row
-    // puts 16 consecutive rows on 16 different 16-byte bank groups (the K
-    // operand reads one chunk of 16 consecutive rows); two slots per V row put
-    // 4 consecutive rows x 32 bytes on distinct banks (the transposed V reads).
+    // Row strides in LDS, in 16-byte slots (LDS serves 256 bytes per cycle).
+    // One slot of padding per K row puts 16 consecutive rows on 16 different
+    // 16-byte bank groups (the K operand reads one chunk of 16 consecutive
+    // rows).  Four slots per V row put 4 consecutive rows x 64 bytes on
+    // distinct banks (the transposed V reads of 32 lanes: 4 key rows x 32
+    // columns).
     static constexpr int KS = CHUNKS + 1;
-    static constexpr int VS = CHUNKS + 2;
+    static constexpr int VS = CHUNKS + 4;
     static constexpr int KTILE = BN * KS * 16;   // bytes per K tile in LDS
     static constexpr int VTILE = BN * VS * 16;
     static constexpr int KLOADS = KTILE / 1024;  // 1 KiB direct loads per K tile
