@@ -296,7 +296,7 @@ def main() -> int:
 # ------------------------------------------------------- counter summaries
 
 def _read_counters(d: str, counter: str) -> dict:
-    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3 --pmc run."""
+    """Per-dispatch values of `counter` (KiB), by kernel name, from a rocprofv3 --pmc run."""
     import csv
 
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -308,25 +308,33 @@ def _read_counters(d: str, counter: str) -> dict:
             if row.get("Counter_Name") != counter:
                 continue
             key = (row.get("Dispatch_Id"), row.get("Kernel_Name"))
-            vals.setdefault(key, 0.0)
-            vals[key] += float(row["Counter_Value"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
     per_kernel: dict = {}
     for (_, name), v in vals.items():
         per_kernel.setdefault(name, []).append(v)
-    return {k: float(np.mean(v)) for k, v in per_kernel.items()}
+    return per_kernel
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per launch of each attention kernel from two counter runs.
+
+    The byte counters are calibrated against the known-size device copy of
+    the --pmc-pass run (its largest copy dispatch moves COPY_BYTES each way):
+    factor = true bytes / counted bytes, applied to every kernel.
+    """
     fetch = _read_counters(fetch_dir, "FETCH_SIZE")
     write = _read_counters(write_dir, "WRITE_SIZE")
-    copy = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy = [k for k in fetch if "copybuffer" in k.lower()]
     if not copy:
         raise SystemExit("copy kernel not found in the FETCH_SIZE run")
-    ck = max(copy, key=lambda k: fetch[k])
-    f_factor = (COPY_BYTES / 1024.0) / fetch[ck]
-    w_factor = (COPY_BYTES / 1024.0) / write.get(ck, float("nan"))
+    ck = copy[0]
+    f_factor = (COPY_BYTES / 1024.0) / max(fetch[ck])
+    w_factor = (COPY_BYTES / 1024.0) / max(write[ck])
     out = {"source_sha256": source_digest(), "copy_kernel": ck, "copy_bytes": COPY_BYTES,
-           "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
+           "fetch_factor": f_factor, "write_factor": w_factor,
+           "command": "rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py --pmc-pass ; "
+                      "the same with --pmc WRITE_SIZE ; python3 bench.py --summarize-pmc <fetch dir> <write dir>",
+           "kernels": {}}
     for name in fetch:
         short = None
         for tag in ("prefill_bf16_kernel<128>", "prefill_bf16_kernel<64>", "decode_split_kernel<128>",
@@ -336,9 +344,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
         if short is None:
             continue
         wl = PREFILL_CONFIG if short.startswith("prefill") else DECODE_CONFIG
-        out["kernels"][short] = {"workload": wl, "fetch_kib_raw": fetch[name], "write_kib_raw": write.get(name),
-                                 "fetch_bytes": fetch[name] * 1024 * f_factor,
-                                 "write_bytes": write.get(name, 0.0) * 1024 * w_factor}
+        fk = float(np.mean(fetch[name]))
+        wk = float(np.mean(write.get(name, [0.0])))
+        out["kernels"][short] = {"workload": wl, "dispatches": len(fetch[name]), "fetch_kib_raw": fk,
+                                 "write_kib_raw": wk, "fetch_bytes": fk * 1024 * f_factor,
+                                 "write_bytes": wk * 1024 * w_factor}
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))
     return 0
