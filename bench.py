@@ -19,6 +19,13 @@ sample of the same prefill workload.
 
 turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 `bench.py --pmc-pass` into profiles/hbm_traffic.json.
+
+    python bench.py --summarize-clock DIR
+
+turns one `rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE` run of
+`bench.py --pmc-pass` into per-kernel GPU cycles, the shader clock the
+kernel actually ran at (cycles / duration) and, for the prefill, the MFMA
+utilisation in cycles: profiles/sclk_prefill_c2_decode_c5.json.
 """
 from __future__ import annotations
 
@@ -44,6 +51,9 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 PREFILL_CONFIG = "c2_causal_b4h16n2048"
 DECODE_CONFIG = "c5_paged_decode_64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "sclk_prefill_c2_decode_c5.json")
+NUM_XCD = 8                   # GRBM_GUI_ACTIVE is counted once per accelerator die
+MFMA_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA, whole GPU, per shader clock
 CSRC = os.path.join(ROOT, "exact_io_aware_fwd_amd", "csrc")
 COPY_BYTES = 1 << 30          # known-size copy used to calibrate the HBM byte counters
 
@@ -166,10 +176,13 @@ def main() -> int:
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for counter collection: a few steps plus one known-size copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-clock", metavar="DIR")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc)
+    if args.summarize_clock:
+        return summarize_clock(args.summarize_clock)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
                                    "this build (--gpus must be 1)"}))
@@ -350,6 +363,56 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
                                  "write_kib_raw": wk, "fetch_bytes": fk * 1024 * f_factor,
                                  "write_bytes": wk * 1024 * w_factor}
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def summarize_clock(d: str) -> int:
+    """Cycles, shader clock and cycle-based MFMA utilisation per attention kernel.
+
+    GRBM_GUI_ACTIVE counts busy GPU cycles per die; per dispatch it is summed
+    over the dies and divided by their number.  The kernel-trace duration of
+    the same dispatch gives the clock it ran at.  MFMA utilisation in cycles
+    = algorithmic flops / (cycles x whole-GPU dense bf16 flops per clock):
+    the fraction of peak the kernel reaches at whatever clock the chip held.
+    """
+    import csv
+
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    counters = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not traces or not counters:
+        raise SystemExit(f"need kernel_trace.csv and counter_collection.csv under {d}")
+    dur, name = {}, {}
+    for f in traces:
+        for row in csv.DictReader(open(f)):
+            dur[row["Dispatch_Id"]] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            name[row["Dispatch_Id"]] = row["Kernel_Name"]
+    cyc: dict = {}
+    for f in counters:
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") == "GRBM_GUI_ACTIVE":
+                cyc[row["Dispatch_Id"]] = cyc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    pc = workloads.prefill_config(PREFILL_CONFIG)
+    flops = prefill_flops(pc)
+    out = {"source_sha256": source_digest(),
+           "command": "rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE -f csv -d <dir> -o run -- "
+                      "python3 bench.py --pmc-pass ; python3 bench.py --summarize-clock <dir>",
+           "kernels": {}}
+    # the combine kernel (~14 us) is too short for the per-die busy counter to
+    # bracket it reliably; only the two long kernels are summarised
+    for tag in ("prefill_bf16_kernel<128>", "decode_split_kernel<128>"):
+        ids = [i for i in dur if tag in name[i] and i in cyc]
+        if not ids:
+            continue
+        c = np.array([cyc[i] / NUM_XCD for i in ids])
+        t = np.array([dur[i] for i in ids], dtype=np.float64)
+        k = {"workload": PREFILL_CONFIG if tag.startswith("prefill") else DECODE_CONFIG,
+             "dispatches": len(ids), "cycles_median": float(np.median(c)),
+             "ns_median": float(np.median(t)), "sclk_ghz_median": float(np.median(c / t))}
+        if tag.startswith("prefill"):
+            k["mfma_util_cycles"] = float(flops / (np.median(c) * MFMA_FLOP_PER_CLK))
+        out["kernels"][tag] = k
+    json.dump(out, open(CLOCK_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))
     return 0
 

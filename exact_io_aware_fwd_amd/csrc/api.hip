@@ -7,6 +7,7 @@
 
 namespace xattn {
 int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+int prefill_bf16_rows_per_block();
 int launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 }  // namespace xattn
 
@@ -57,7 +58,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (q == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
     if (Nk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARGUMENT;
-    const long long tiles = (Nq + 127) / 128;
+    const long long rows_per_block = dtype == ATTN_DTYPE_BF16 ? xattn::prefill_bf16_rows_per_block() : 128;
+    const long long tiles = (Nq + rows_per_block - 1) / rows_per_block;
     if ((long long)B * Hq * tiles > kMaxGrid) return ATTN_ERR_UNSUPPORTED;
 
     xattn::PrefillParams p;

@@ -11,9 +11,9 @@
 // Both contractions run on the matrix cores with v_mfma_f32_32x32x16_bf16 and
 // fp32 accumulation.  They are evaluated transposed, S^T = K Q^T and
 // O^T = V^T P^T, because that MFMA's accumulator layout puts one query row's
-// scores in a single lane pair (lane l and lane l ^ 32): the row max needs one
-// cross-lane exchange per tile and the per-row rescale factor is a per-lane
-// scalar.  The S^T accumulator registers are exactly the P^T operand of the
+// scores in a single lane pair (lane l and lane l ^ 32): the row max needs at
+// most one cross-lane exchange per tile and the per-row rescale factor is a
+// per-lane scalar.  The S^T accumulator registers are exactly the P^T operand of the
 // second MFMA once converted to bf16, up to a fixed permutation of the keys
 // inside each 16-key block, which the V^T tile in LDS is stored with.
 //
@@ -130,14 +130,20 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
                 if (key < lo_i || key > hi_i) s[jb][r] = neg_inf();
             }
     }
-    // ---- online softmax (base 2) with conditional rescaling
-    float mt = neg_inf();
+    // Row max: each lane reduces its own half of the row (two independent
+    // chains, a dependent VALU op waits a second issue slot).  Weights stay
+    // relative to the running max m_run unless some half-row exceeds it by
+    // more than the threshold; only then are the two halves combined (the one
+    // cross-lane exchange) and the accumulator rescaled to the new row max.
+    float ma = neg_inf(), mb = neg_inf();
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[jb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mt > st.m_run + kRescaleThreshold)) {
+    for (int r = 0; r < 16; ++r) {
+        ma = fmaxf(ma, s[0][r]);
+        mb = fmaxf(mb, s[1][r]);
+    }
+    const float mh = fmaxf(ma, mb) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mh > st.m_run + kRescaleThreshold)) {
+        const float mt = fmaxf(mh, __shfl_xor(mh, 32));
         // A row that has still seen no key (both maxima -inf) keeps alpha = 0
         // from the 0 reference instead of exp2(-inf - -inf) = NaN; its acc and
         // sums are 0 anyway.
@@ -150,21 +156,22 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
         st.m_run = m_new;
     }
     const float m_use = st.m_run == neg_inf() ? 0.f : st.m_run;
-    float fsum = 0.f;
+    float fs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], scale_log2, -m_use));
-            fsum += s[jb][r];
+            fs[(r & 1) + 2 * jb] += s[jb][r];
         }
+    const float fsum = (fs[0] + fs[1]) + (fs[2] + fs[3]);
     // P^T operands (bf16), one per 16-key block.  O is normalised by the sum of
     // the same bf16-rounded weights the PV product uses, so it is an exact
     // weighted average of V rows under those weights (a dot with (1, 1) adds
     // two packed bf16 values at once); the LSE uses the fp32 sum, free of the
     // weights' rounding.
     bf16x8 pf[4];
-    float psum = 0.f;
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int jb = kb >> 1, h = (kb & 1) * 8;
@@ -172,11 +179,11 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             w[e] = pack_bf16x2(s[jb][h + 2 * e], s[jb][h + 2 * e + 1]);
-            psum = sum_bf16x2(w[e], psum);
+            ps[e & 1] = sum_bf16x2(w[e], ps[e & 1]);
         }
         pf[kb] = __builtin_bit_cast(bf16x8, w);
     }
-    st.l_run += psum;
+    st.l_run += ps[0] + ps[1];
     st.l_f32 += fsum;
     // ---- O^T += V^T P^T.  The V^T operand comes from the row-major V tile
     // through two transposing reads (ds_read_b64_tr_b16): in each 16-lane
@@ -311,6 +318,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
         }
     }
 }
+
+int prefill_bf16_rows_per_block() { return PrefillBf16Cfg<128>::BM; }
 
 int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
     const int blocks = p.B * p.Hq * p.num_q_tiles;
