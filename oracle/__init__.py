@@ -10,6 +10,7 @@ from .attention import (  # noqa: F401
     from_bf16_bits,
     gather_sequence,
     paged_decode,
+    paged_prefill,
     to_f64,
     visibility,
 )

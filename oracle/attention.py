@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for exact attention (prefill) and paged decode.
+"""Plain fp64 CPU oracle for exact attention (prefill), paged decode and
+chunked prefill over a paged cache.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module; only the test suite, the smoke check and the benchmark's
@@ -176,3 +177,52 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
         out_o[n] = o[0, :, 0, :]
         out_l[n] = lse[0, :, 0]
     return out_o, out_l
+
+
+def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                  seq_lens: np.ndarray, q_offsets: np.ndarray, scale: float, mask: str = "causal",
+                  window: int = 0, seqs=None, dtype: str = "f64"):
+    """Chunked prefill over a paged KV cache, in float64.
+
+    The serving pattern that pairs a tiled attention kernel with KV paging
+    (the FlashAttention serving-value question page, Real-world examples;
+    paged kernels, "Attention and matrix kernels" page).  Sequence s holds
+    seq_lens[s] cached tokens, the newest Nq_s = q_offsets[s+1] - q_offsets[s]
+    of which are the chunk being prefilled; its queries are the token-major
+    rows q[q_offsets[s]:q_offsets[s+1]] of q [total_q, Hq, d].  Query i of a
+    chunk sits at key position i + seq_len - Nq_s (bottom-right alignment),
+    so under the causal mask it sees keys 0 .. i + seq_len - Nq_s.
+
+    Each sequence's K and V are gathered through its block table into
+    contiguous arrays and handed to ``attention`` with Nq = Nq_s, Nk =
+    seq_len.  Returns o [total_q', Hq, d] and lse [total_q', Hq] for the
+    tokens of the sequences ``seqs`` (default: all), in their order.
+    ``dtype="bf16"``: q and the pages are raw bf16 bit patterns.
+    """
+    q = to_f64(q, dtype) if dtype == "bf16" else np.asarray(q, dtype=np.float64)
+    T, Hq, d = q.shape
+    offs = np.asarray(q_offsets, dtype=np.int64)
+    S = offs.size - 1
+    seqs = range(S) if seqs is None else list(seqs)
+    outs_o, outs_l = [], []
+    for s in seqs:
+        a, b = int(offs[s]), int(offs[s + 1])
+        n, L = b - a, int(seq_lens[s])
+        o = np.zeros((n, Hq, d), dtype=np.float64)
+        lse = np.full((n, Hq), -np.inf, dtype=np.float64)
+        if n > 0 and L > 0:
+            ks = gather_sequence(k_pages, block_table[s], L)
+            vs = gather_sequence(v_pages, block_table[s], L)
+            if dtype == "bf16":
+                ks, vs = from_bf16_bits(ks), from_bf16_bits(vs)
+            else:
+                ks, vs = ks.astype(np.float64), vs.astype(np.float64)
+            qs = np.transpose(q[a:b], (1, 0, 2))[None]          # [1, Hq, n, d]
+            os_, ls_ = attention(qs, ks[None], vs[None], scale, mask, window)
+            o = np.transpose(os_[0], (1, 0, 2))
+            lse = np.transpose(ls_[0], (1, 0))
+        outs_o.append(o)
+        outs_l.append(lse)
+    if not outs_o:
+        return np.zeros((0, Hq, d)), np.zeros((0, Hq))
+    return np.concatenate(outs_o, axis=0), np.concatenate(outs_l, axis=0)

@@ -353,3 +353,109 @@ def test_generated_decode_layout_matches_oracle_gather():
     o, lse = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
                                  c["scale"], dtype="bf16")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ------------------------------------------------ chunked prefill over pages
+
+def _build_paged(conts, P, rng, fill=np.nan):
+    """Page the contiguous [Hkv, n, d] K/V of each sequence through one random permutation."""
+    lens = [c[0].shape[1] for c in conts]
+    Hkv, d = conts[0][0].shape[0], conts[0][0].shape[2]
+    npages = max(1, sum(-(-n // P) for n in lens))
+    perm = rng.permutation(npages)
+    kp = np.full((npages, Hkv, P, d), fill)
+    vp = np.full((npages, Hkv, P, d), fill)
+    bt = np.full((len(lens), max(1, max(-(-n // P) for n in lens))), -1, dtype=np.int32)
+    g = 0
+    for s, n in enumerate(lens):
+        for p in range(-(-n // P)):
+            phys = perm[g]
+            g += 1
+            bt[s, p] = phys
+            m = min(P, n - p * P)
+            kp[phys, :, :m] = conts[s][0][:, p * P:p * P + m]
+            vp[phys, :, :m] = conts[s][1][:, p * P:p * P + m]
+    return kp, vp, bt
+
+
+def _brute_paged_prefill(q, kp, vp, bt, lens, offs, scale, mask, window):
+    """50-digit reference read token by token through the block table (no gather)."""
+    mpmath.mp.dps = 50
+    T, Hq, d = q.shape
+    Hkv, P = kp.shape[1], kp.shape[2]
+    g = Hq // Hkv
+    O = np.zeros(q.shape)
+    L = np.full((T, Hq), -np.inf)
+    for s in range(len(lens)):
+        n, Ls = offs[s + 1] - offs[s], lens[s]
+        for i in range(n):
+            keys = _visible_keys(i, n, Ls, mask, window, None)
+            for h in range(Hq):
+                if not keys:
+                    continue
+                hk = h // g
+                kv = {j: (kp[bt[s, j // P], hk, j % P], vp[bt[s, j // P], hk, j % P]) for j in keys}
+                sc = {j: mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[offs[s] + i, h, c]) * mpmath.mpf(kv[j][0][c])
+                                                         for c in range(d)) for j in keys}
+                w = {j: mpmath.exp(sc[j]) for j in keys}
+                tot = mpmath.fsum(w.values())
+                for c in range(d):
+                    O[offs[s] + i, h, c] = float(mpmath.fsum(w[j] * mpmath.mpf(kv[j][1][c]) for j in keys) / tot)
+                L[offs[s] + i, h] = float(mpmath.log(tot))
+    return O, L
+
+
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("none", 0), ("window", 4)])
+def test_paged_prefill_brute_force_tiny(mask, window):
+    # chunk < context, chunk = context, a single new token, and a chunk longer
+    # than an empty context (its rows see nothing)
+    Hq, Hkv, d, P = 4, 2, 3, 16
+    lens, chunks = [20, 5, 33, 0], [3, 5, 1, 2]
+    rng = np.random.default_rng(61)
+    conts = [(rng.standard_normal((Hkv, n, d)), rng.standard_normal((Hkv, n, d))) for n in lens]
+    kp, vp, bt = _build_paged(conts, P, rng)
+    offs = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((offs[-1], Hq, d))
+    o, lse = oracle.paged_prefill(q, kp, vp, bt, np.array(lens), offs, 0.6, mask, window)
+    ob, lb = _brute_paged_prefill(q, kp, vp, bt, lens, offs, 0.6, mask, window)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    fin = np.isfinite(lb)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-13)
+    assert np.all(o[~fin] == 0.0)
+    assert not fin[offs[3]:].any()     # empty context: no key for any row
+
+
+def test_paged_prefill_single_token_chunks_equal_decode():
+    c = workloads.make_decode(5, 8, 2, 16, len_min=3, len_max=90, seed=8, tail_fill="nan")
+    offs = np.arange(6)
+    od, ld = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                 c["scale"], dtype="bf16")
+    op, lp = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"], offs,
+                                  c["scale"], "causal", dtype="bf16")
+    np.testing.assert_array_equal(op, od)
+    np.testing.assert_array_equal(lp, ld)
+
+
+def test_paged_prefill_ignores_page_placement():
+    Hq, Hkv, d, P = 4, 1, 5, 16
+    lens, chunks = [40, 17], [12, 17]
+    rng = np.random.default_rng(5)
+    conts = [(rng.standard_normal((Hkv, n, d)), rng.standard_normal((Hkv, n, d))) for n in lens]
+    offs = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((offs[-1], Hq, d))
+    res = []
+    for seed in (1, 2):
+        kp, vp, bt = _build_paged(conts, P, np.random.default_rng(seed))
+        res.append(oracle.paged_prefill(q, kp, vp, bt, np.array(lens), offs, 0.4))
+    np.testing.assert_allclose(res[0][0], res[1][0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(res[0][1], res[1][1], rtol=0, atol=1e-15)
+
+
+def test_generated_chunked_layout_is_nan_safe():
+    c = workloads.make_chunked_prefill(3, 4, 2, 16, prefix_min=0, prefix_max=40, chunk_min=1, chunk_max=30,
+                                       seed=4, tail_fill="nan")
+    o, lse = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                  c["q_offsets"], c["scale"], "causal", dtype="bf16")
+    assert o.shape == (int(c["q_offsets"][-1]), 4, 16)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))

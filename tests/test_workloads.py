@@ -52,3 +52,27 @@ def test_decode_generator_layout():
         tail = int(n) % 16
         if tail:
             assert np.all(c["k_pages"][last, :, tail:] == 0)
+
+
+def test_chunked_prefill_structure():
+    c = workloads.make_chunked_prefill(6, 4, 2, 16, prefix_min=0, prefix_max=100, chunk_min=1, chunk_max=40,
+                                       seed=2, tail_fill="nan")
+    offs, lens, bt = c["q_offsets"], c["seq_lens"], c["block_table"]
+    chunks = np.diff(offs)
+    assert offs[0] == 0 and np.all(chunks >= 1) and c["q"].shape == (offs[-1], 4, 16)
+    assert np.all(lens >= chunks) and c["max_q_len"] == chunks.max()
+    P = c["page_size"]
+    used = np.concatenate([bt[s, :-(-int(n) // P)] for s, n in enumerate(lens)])
+    assert used.size == c["k_pages"].shape[0] and np.unique(used).size == used.size   # each page once
+    for s, n in enumerate(lens):
+        assert np.all(bt[s, -(-int(n) // P):] == -1)
+        if n % P:   # slots past the end hold the NaN fill
+            tail = c["k_pages"][bt[s, n // P], :, n % P:, :]
+            assert np.all(tail == workloads.gen.BF16_QNAN)
+
+
+def test_chunked_config_c6_shape():
+    c = workloads.chunked_config("c6_chunked_prefill_16")
+    assert c["q_offsets"][-1] == c["q"].shape[0] and c["num_seqs"] == 16
+    assert c["k_pages"].shape[1:] == (8, 16, 128)
+    assert int(c["max_seq_len"]) == int(c["seq_lens"].max())

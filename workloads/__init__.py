@@ -13,4 +13,6 @@ from .gen import (  # noqa: F401
     make_prefill,
     prefill_config,
     decode_config,
+    make_chunked_prefill,
+    chunked_config,
 )

@@ -42,6 +42,10 @@ CONFIGS = {
                                dtype="bf16", mask="document", doc_min=512, doc_max=8192),
     "c5_paged_decode_64": dict(kind="decode", num_seqs=64, Hq=32, Hkv=8, d=128, page_size=16,
                                len_min=1024, len_max=32768),
+    # chunked prefill: each sequence prefills a chunk of new tokens against a
+    # cached prefix, all through the paged cache
+    "c6_chunked_prefill_16": dict(kind="chunked", num_seqs=16, Hq=32, Hkv=8, d=128, page_size=16,
+                                  prefix_min=0, prefix_max=8192, chunk_min=256, chunk_max=2048),
 }
 
 
@@ -195,6 +199,44 @@ def make_decode(num_seqs: int, Hq: int, Hkv: int, d: int, *, page_size: int = 16
                 dtype="bf16")
 
 
+def make_chunked_prefill(num_seqs: int, Hq: int, Hkv: int, d: int, *, page_size: int = 16,
+                         prefix_min: int = 0, prefix_max: int = 8192, chunk_min: int = 256,
+                         chunk_max: int = 2048, seed: int = 0, chunks: list[int] | None = None,
+                         prefixes: list[int] | None = None, tail_fill: str = "zero",
+                         extra_pages: int = 0, scale: float | None = None) -> dict:
+    """Draw one chunked-prefill problem over a paged cache (bf16 only).
+
+    Sequence s has a cached prefix of prefixes[s] tokens and a chunk of
+    chunks[s] new tokens (uniform in [prefix_min, prefix_max] and [chunk_min,
+    chunk_max] unless given, drawn from the generator seeded (seed, 6): chunk
+    lengths first, then prefixes).  The chunk's own K and V are already in the
+    cache, so seq_lens = prefix + chunk; the cache (pages, block table, tail
+    fill) is the one make_decode draws for those lengths.  The queries are the
+    chunk tokens, token-major q [sum(chunks), Hq, d] (stream 4), with
+    q_offsets [num_seqs + 1] the running sums of the chunk lengths.
+    """
+    rng = np.random.default_rng([seed, 6])
+    if chunks is None:
+        chunks = rng.integers(chunk_min, chunk_max + 1, num_seqs).tolist()
+    if prefixes is None:
+        prefixes = rng.integers(prefix_min, prefix_max + 1, num_seqs).tolist()
+    chunks = [int(x) for x in chunks]
+    prefixes = [int(x) for x in prefixes]
+    assert len(chunks) == num_seqs and len(prefixes) == num_seqs
+    lens = [a + b for a, b in zip(prefixes, chunks)]
+    cache = make_decode(num_seqs, Hq, Hkv, d, page_size=page_size, seed=seed, seq_lens=lens,
+                        max_seq_len=max(lens) if lens else 0, tail_fill=tail_fill,
+                        extra_pages=extra_pages, scale=scale)
+    q_offsets = np.zeros(num_seqs + 1, dtype=np.int32)
+    q_offsets[1:] = np.cumsum(chunks)
+    q = _draw(seed, 4, (int(q_offsets[-1]), Hq, d), "bf16")
+    return dict(kind="chunked", q=q, k_pages=cache["k_pages"], v_pages=cache["v_pages"],
+                block_table=cache["block_table"], seq_lens=cache["seq_lens"], q_offsets=q_offsets,
+                num_seqs=num_seqs, Hq=Hq, Hkv=Hkv, d=d, page_size=page_size,
+                max_seq_len=cache["max_seq_len"], max_q_len=max(chunks) if chunks else 0,
+                scale=cache["scale"], dtype="bf16", mask="causal", window=0)
+
+
 def prefill_config(name: str, seed: int = 0) -> dict:
     c = dict(CONFIGS[name])
     assert c.pop("kind") == "prefill"
@@ -206,3 +248,10 @@ def decode_config(name: str, seed: int = 0, **overrides) -> dict:
     assert c.pop("kind") == "decode"
     c.update(overrides)
     return make_decode(seed=seed, **c)
+
+
+def chunked_config(name: str, seed: int = 0, **overrides) -> dict:
+    c = dict(CONFIGS[name])
+    assert c.pop("kind") == "chunked"
+    c.update(overrides)
+    return make_chunked_prefill(seed=seed, **c)
