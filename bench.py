@@ -25,7 +25,8 @@ turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 turns one `rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE` run of
 `bench.py --pmc-pass` into per-kernel GPU cycles, the shader clock the
 kernel actually ran at (cycles / duration) and, for the prefill, the MFMA
-utilisation in cycles: profiles/sclk_prefill_c2_decode_c5.json.
+utilisation in cycles (prefill C2, decode C5, chunked prefill C6):
+profiles/sclk_prefill_c2_decode_c5.json.
 """
 from __future__ import annotations
 
@@ -50,6 +51,7 @@ PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/cl
 PEAK_HBM_GBS = 8000.0         # HBM3E
 PREFILL_CONFIG = "c2_causal_b4h16n2048"
 DECODE_CONFIG = "c5_paged_decode_64"
+CHUNKED_CONFIG = "c6_chunked_prefill_16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "sclk_prefill_c2_decode_c5.json")
 NUM_XCD = 8                   # GRBM_GUI_ACTIVE is counted once per accelerator die
@@ -86,6 +88,18 @@ def visible_pairs(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None
 
 def prefill_flops(c: dict) -> int:
     return 4 * c["d"] * c["B"] * c["Hq"] * visible_pairs(c["Nq"], c["Nk"], c["mask"], c["window"], c["doc_offsets"])
+
+
+def chunked_visible_pairs(c: dict) -> int:
+    """Visible (query, key) pairs of a chunked prefill, per query head: chunk s
+    is a problem with Nq = chunk length and Nk = cached length (bottom-right)."""
+    offs = np.asarray(c["q_offsets"], dtype=np.int64)
+    return sum(visible_pairs(int(offs[s + 1] - offs[s]), int(c["seq_lens"][s]), c["mask"], c["window"])
+               for s in range(c["num_seqs"]))
+
+
+def chunked_flops(c: dict) -> int:
+    return 4 * c["d"] * c["Hq"] * chunked_visible_pairs(c)
 
 
 def prefill_bytes(c: dict) -> int:
@@ -173,6 +187,7 @@ def main() -> int:
     ap.add_argument("--prefill-config", default=PREFILL_CONFIG)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for counter collection: a few steps plus one known-size copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -225,6 +240,8 @@ def main() -> int:
             prefill()
             decode()
         torch.cuda.synchronize()
+        if not args.no_chunked:
+            time_chunked(3, 0)
         log("pmc pass done")
         return 0
 
@@ -299,11 +316,50 @@ def main() -> int:
                          "kernel": "decode_split_kernel<128> + decode_combine_kernel<128> (one call)"},
         },
     }
+    if not args.no_chunked:
+        result["chunked_prefill"] = time_chunked(K, W)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(pc, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_chunked(K: int, W: int) -> dict:
+    """Chunked prefill over the paged cache (its own workload, timed alone
+    after the step loop): algorithmic TFLOP/s against the bf16 MFMA peak."""
+    import torch
+    from exact_io_aware_fwd_amd import attn_paged_prefill
+
+    c = workloads.chunked_config(CHUNKED_CONFIG)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    q, kp, vp = to_dev(c["q"]), to_dev(c["k_pages"]), to_dev(c["v_pages"])
+    bt, sl, qo = i32(c["block_table"]), i32(c["seq_lens"]), i32(c["q_offsets"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def call():
+        attn_paged_prefill(q, kp, vp, bt, sl, qo, max_seq_len=c["max_seq_len"], max_q_len=c["max_q_len"],
+                           scale=c["scale"], mask=c["mask"], out=o, lse=lse)
+
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    flops = chunked_flops(c)
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"chunked prefill: {us:.1f} us, {tf:.1f} TFLOP/s")
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "us": round(us, 2), "flop_per_call": flops,
+            "workload": f"{CHUNKED_CONFIG} ({c['num_seqs']} seqs, Hq{c['Hq']} Hkv{c['Hkv']} d{c['d']}, "
+                        f"{int(c['q_offsets'][-1])} chunk tokens over {int(c['seq_lens'].sum())} cached, causal)",
+            "kernel": f"paged_prefill_bf16_kernel<{c['d']}>"}
 
 
 # ------------------------------------------------------- counter summaries
@@ -351,12 +407,13 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
     for name in fetch:
         short = None
         for tag in ("prefill_bf16_kernel<128>", "prefill_bf16_kernel<64>", "decode_split_kernel<128>",
-                    "decode_combine_kernel<128>"):
-            if tag in name:
+                    "decode_combine_kernel<128>", "paged_prefill_bf16_kernel<128>"):
+            if tag in name and (short is None or len(tag) > len(short)):
                 short = tag
         if short is None:
             continue
-        wl = PREFILL_CONFIG if short.startswith("prefill") else DECODE_CONFIG
+        wl = (CHUNKED_CONFIG if short.startswith("paged") else
+              PREFILL_CONFIG if short.startswith("prefill") else DECODE_CONFIG)
         fk = float(np.mean(fetch[name]))
         wk = float(np.mean(write.get(name, [0.0])))
         out["kernels"][short] = {"workload": wl, "dispatches": len(fetch[name]), "fetch_kib_raw": fk,
@@ -392,25 +449,27 @@ def summarize_clock(d: str) -> int:
         for row in csv.DictReader(open(f)):
             if row.get("Counter_Name") == "GRBM_GUI_ACTIVE":
                 cyc[row["Dispatch_Id"]] = cyc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    pc = workloads.prefill_config(PREFILL_CONFIG)
-    flops = prefill_flops(pc)
+    flops = {"prefill_bf16_kernel<128>": prefill_flops(workloads.prefill_config(PREFILL_CONFIG)),
+             "paged_prefill_bf16_kernel<128>": chunked_flops(workloads.chunked_config(CHUNKED_CONFIG))}
     out = {"source_sha256": source_digest(),
            "command": "rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE -f csv -d <dir> -o run -- "
                       "python3 bench.py --pmc-pass ; python3 bench.py --summarize-clock <dir>",
            "kernels": {}}
     # the combine kernel (~14 us) is too short for the per-die busy counter to
     # bracket it reliably; only the two long kernels are summarised
-    for tag in ("prefill_bf16_kernel<128>", "decode_split_kernel<128>"):
-        ids = [i for i in dur if tag in name[i] and i in cyc]
+    workload = {"prefill_bf16_kernel<128>": PREFILL_CONFIG, "decode_split_kernel<128>": DECODE_CONFIG,
+                "paged_prefill_bf16_kernel<128>": CHUNKED_CONFIG}
+    for tag, wl in workload.items():
+        # kernel names are demangled signatures: match the name, not a prefix of another
+        ids = [i for i in dur if f"::{tag}(" in name[i] and i in cyc]
         if not ids:
             continue
         c = np.array([cyc[i] / NUM_XCD for i in ids])
         t = np.array([dur[i] for i in ids], dtype=np.float64)
-        k = {"workload": PREFILL_CONFIG if tag.startswith("prefill") else DECODE_CONFIG,
-             "dispatches": len(ids), "cycles_median": float(np.median(c)),
+        k = {"workload": wl, "dispatches": len(ids), "cycles_median": float(np.median(c)),
              "ns_median": float(np.median(t)), "sclk_ghz_median": float(np.median(c / t))}
-        if tag.startswith("prefill"):
-            k["mfma_util_cycles"] = float(flops / (np.median(c) * MFMA_FLOP_PER_CLK))
+        if tag in flops:
+            k["mfma_util_cycles"] = float(flops[tag] / (np.median(c) * MFMA_FLOP_PER_CLK))
         out["kernels"][tag] = k
     json.dump(out, open(CLOCK_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))

@@ -3,5 +3,5 @@
 The computation lives in the HIP library libexact_attn.so (C ABI declared in
 include/exact_attn.h); this package is its thin Python binding.
 """
-from .api import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size  # noqa: F401
+from .api import attn_fwd, attn_paged_decode, attn_paged_decode_workspace_size, attn_paged_prefill  # noqa: F401
 from ._lib import AttnError, LIB_PATH, lib, status_string  # noqa: F401

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
     L.attn_paged_decode_workspace_size.restype = sz
     L.attn_paged_decode.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, p, sz, p]
     L.attn_paged_decode.restype = i
+    L.attn_paged_prefill.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, AttnMask, p]
+    L.attn_paged_prefill.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L

@@ -106,3 +106,37 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                       float(scale), ctypes_ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st)
     return out, lse
+
+
+def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                       block_table: torch.Tensor, seq_lens: torch.Tensor, q_offsets: torch.Tensor, *,
+                       max_seq_len: int, max_q_len: int, scale: float | None = None, mask: str = "causal",
+                       window: int = 0, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       with_lse: bool = True, stream=None):
+    """Chunked prefill over the paged cache: q [T,Hq,d] token-major, pages [P,Hkv,16,d],
+    q_offsets [S+1] -> (o [T,Hq,d] bf16, lse [T,Hq] fp32)."""
+    _need(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad shapes")
+    _need(q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16,
+          "paged prefill is bf16")
+    _need(all(t.dtype == torch.int32 for t in (block_table, seq_lens, q_offsets)),
+          "block_table/seq_lens/q_offsets must be int32")
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k_pages, v_pages, block_table, seq_lens, q_offsets)),
+          "inputs must be contiguous device tensors")
+    T, Hq, d = q.shape
+    _, Hkv, page_size, _ = k_pages.shape
+    S = seq_lens.shape[0]
+    _need(block_table.dim() == 2 and block_table.shape[0] == S and q_offsets.shape == (S + 1,), "index shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    m = make_mask(mask, window)
+    st = _lib.lib().attn_paged_prefill(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
+                                       ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(q_offsets),
+                                       ctypes_ptr(out), None if lse is None else ctypes_ptr(lse),
+                                       S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
+                                       int(max_q_len), float(scale), m, _stream(stream))
+    _lib.check(st)
+    return out, lse

@@ -9,6 +9,7 @@ namespace xattn {
 int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
 int prefill_bf16_rows_per_block();
 int launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
+int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t stream);
 }  // namespace xattn
 
 #include "decode_params.hpp"
@@ -120,5 +121,47 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
     p.scale_log2 = scale * xattn::kLog2e;
     p.ws_o = nullptr; p.ws_lse = nullptr;
     xattn::launch_decode(p, d, max_seq_len, workspace, stream);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_offsets,
+                                  void* o, float* lse,
+                                  int num_seqs, int Hq, int Hkv, int d, int page_size,
+                                  int max_pages_per_seq, int max_seq_len, int max_q_len, float scale,
+                                  attn_mask mask, hipStream_t stream) {
+    if (num_seqs < 0 || Hq < 0 || Hkv < 0 || d < 0 || max_pages_per_seq < 0 || max_seq_len < 0 || max_q_len < 0)
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind < ATTN_MASK_NONE || mask.kind > ATTN_MASK_DOCUMENT) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_DOCUMENT) return ATTN_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)max_pages_per_seq * page_size < max_seq_len) return ATTN_ERR_INVALID_ARGUMENT;
+    if (max_seq_len > kMaxSeq || max_q_len > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * Hq * max_q_len == 0) return ATTN_OK;   // no query row
+    if (q == nullptr || o == nullptr || seq_lens == nullptr || q_offsets == nullptr)
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (max_seq_len > 0 && (k_pages == nullptr || v_pages == nullptr || block_table == nullptr))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    const long long rows_per_block = xattn::prefill_bf16_rows_per_block();
+    const long long tiles = (max_q_len + rows_per_block - 1) / rows_per_block;
+    if ((long long)num_seqs * Hq * tiles > kMaxGrid) return ATTN_ERR_UNSUPPORTED;
+
+    xattn::PagedPrefillParams p;
+    p.q = (const uint16_t*)q; p.k_pages = (const uint16_t*)k_pages; p.v_pages = (const uint16_t*)v_pages;
+    p.block_table = block_table; p.seq_lens = seq_lens; p.q_offsets = q_offsets;
+    p.o = (uint16_t*)o; p.lse = lse;
+    p.num_seqs = num_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+    p.max_pages = max_pages_per_seq;
+    p.num_q_tiles = (int)tiles;
+    p.scale_log2 = scale * xattn::kLog2e;
+    p.mask_kind = mask.kind;
+    p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.window : 0;
+    xattn::launch_paged_prefill_bf16(p, d, stream);
     return hip_status(hipGetLastError());
 }

@@ -38,6 +38,25 @@ struct PrefillParams {
     int num_q_tiles;
 };
 
+// Arguments of one chunked-prefill launch over the paged cache (validated on
+// the host).  Queries, outputs and LSEs are token-major: row t of q is token
+// t of the concatenated chunks, [total_q, Hq, d].
+struct PagedPrefillParams {
+    const uint16_t* q;
+    const uint16_t* k_pages;    // [num_pages, Hkv, 16, d]
+    const uint16_t* v_pages;
+    const int32_t* block_table; // [num_seqs, max_pages]
+    const int32_t* seq_lens;    // [num_seqs]: cached tokens, the chunk included
+    const int32_t* q_offsets;   // [num_seqs + 1]: chunk s is rows q_offsets[s] .. q_offsets[s+1]
+    uint16_t* o;
+    float* lse;                 // [total_q, Hq] or null
+    int num_seqs, Hq, Hkv, group, max_pages;
+    int num_q_tiles;            // query tiles of the longest chunk
+    float scale_log2;
+    int mask_kind;              // none, causal or window
+    int window;
+};
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -94,6 +113,30 @@ __device__ __forceinline__ void decode_work(int id, int nbk, int nqt, int group,
     }
     g = r % group;
     qt = nqt - 1 - qrev;
+}
+
+// Workgroup id -> (sequence * Hkv + kv head, q tile, head within the group)
+// for chunked prefill over the paged cache.  All workgroups of one (sequence,
+// KV head) pair are issued together, on one die, so that pair's cached K/V
+// (which every query tile and every head of the group re-reads) is fetched
+// from HBM about once and then served from that die's L2.  With the query-
+// tile-major order of decode_work a die would cycle through all its pairs'
+// caches at once, far more than its L2 holds.  Pairs are dealt to the dies
+// round-robin (pair x, x + 8, ... on die x) when they divide evenly.
+__device__ __forceinline__ void decode_work_pair_major(int id, int nbk, int nqt, int group,
+                                                       int& bk, int& qt, int& g) {
+    const int per_pair = nqt * group;
+    int r;
+    if (nbk % kNumXcd == 0) {
+        const int x = id % kNumXcd, u = id / kNumXcd;
+        bk = (u / per_pair) * kNumXcd + x;
+        r = u % per_pair;
+    } else {
+        bk = id / per_pair;
+        r = id % per_pair;
+    }
+    qt = nqt - 1 - r / group;   // within a pair, the later (heavier) query tiles first
+    g = r % group;
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -319,6 +319,203 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     }
 }
 
+// ------------------------------------------------------------------------
+// Chunked prefill over the paged KV cache.  The tile compute is tile_step
+// above; what changes is where rows come from.  Query rows are the chunk's
+// tokens (token-major), and a 64-key K/V tile is four 16-token pages that
+// the block table scatters over the page pool, so the copies gather rows
+// with per-lane 64-bit addresses (global_load_lds_dwordx4: lane l's 16 bytes
+// still land at LDS base + 16 l).  Rows at or past the sequence's end read
+// this all-zero row instead, so a page tail's contents (any bit pattern,
+// NaN included) never reach P V: its keys are masked and its values are 0.
+__device__ __attribute__((aligned(16))) uint16_t kZeroRow[128];
+
+// (row, chunk) of the padded tile layout that each of this wave's direct
+// loads fills for this lane (see tile_src_offsets), packed as row << 8 | chunk.
+template <int D, int S, int NL>
+__device__ __forceinline__ void tile_rows_chunks(uint32_t (&rc)[(NL + 3) / 4], int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < (NL + 3) / 4; ++j) {
+        const int slot = (wave + 4 * j) * 64 + lane;
+        const int r = slot / S;
+        int c = slot % S;
+        c = c < D / 8 ? c : D / 8 - 1;
+        rc[j] = (uint32_t)((r << 8) | c);
+    }
+}
+
+// Issue this wave's copies of one 64-key tile.  pb0..pb3: element offsets in
+// the page pool of the tile's four pages for this KV head; `rows` = keys of
+// the tile that exist (rows at or past it read the zero row).
+template <int D, int NL>
+__device__ __forceinline__ void load_paged_tile_async(const uint16_t* __restrict__ pool, size_t pb0, size_t pb1,
+                                                      size_t pb2, size_t pb3, int rows, uint8_t* lds,
+                                                      const uint32_t (&rc)[(NL + 3) / 4], int wave) {
+#pragma unroll
+    for (int j = 0; j < (NL + 3) / 4; ++j) {
+        const int blk = wave + 4 * j;
+        if (NL % 4 == 0 || blk < NL) {
+            const int r = (int)(rc[j] >> 8), c = (int)(rc[j] & 255);
+            const size_t pb = r < 32 ? (r < 16 ? pb0 : pb1) : (r < 48 ? pb2 : pb3);
+            const uint16_t* src = r < rows ? pool + pb + (size_t)((r & 15) * D + c * 8) : kZeroRow + c * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + blk * 1024), 16, 0, 0);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefillParams pp) {
+    using C = PrefillBf16Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[C::VTILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bk, qt, g;
+    decode_work_pair_major(blockIdx.x, pp.num_seqs * pp.Hkv, pp.num_q_tiles, pp.group, bk, qt, g);
+    const int seq = bk / pp.Hkv, hkv = bk % pp.Hkv, hq = hkv * pp.group + g;
+    const int q0 = pp.q_offsets[seq];
+    const int nq = pp.q_offsets[seq + 1] - q0;   // chunk length
+    const int L = pp.seq_lens[seq];              // cached keys, the chunk included
+    const int r0 = qt * C::BM;
+    if (r0 >= nq) return;                        // whole workgroup: this chunk is shorter
+
+    // the sequence as one attention problem: Nq = chunk, Nk = cache length,
+    // bottom-right alignment (row_interval puts query i at i + Nk - Nq)
+    PrefillParams p;
+    p.Nq = nq;
+    p.Nk = L;
+    p.mask_kind = pp.mask_kind;
+    p.window = pp.window;
+    p.doc_offsets = nullptr;
+    p.num_docs = 0;
+
+    const int r_last = min(r0 + C::BM, nq) - 1;
+    const int w0 = r0 + wave * 32;
+    const int w_last = min(w0 + 31, nq - 1);
+    const int row = w0 + (lane & 31);
+    const bool row_ok = row < nq;
+
+    int lo_i, hi_i;
+    row_interval(p, row, lo_i, hi_i);
+    int lo_wg, tmp, hi_wg;
+    row_interval(p, r0, lo_wg, tmp);
+    row_interval(p, r_last, tmp, hi_wg);
+    int lo_w_first, hi_w_first, lo_w_last, hi_w_last;
+    row_interval(p, w0, lo_w_first, hi_w_first);
+    row_interval(p, w_last, lo_w_last, hi_w_last);
+    const bool wave_has_rows = w0 < nq;
+
+    const size_t row_stride = (size_t)pp.Hq * D;   // token-major rows
+    PrefillBf16State<D> st;
+    {
+        const uint16_t* qrow = pp.q + (size_t)(q0 + (row_ok ? row : 0)) * row_stride + (size_t)hq * D;
+#pragma unroll
+        for (int kk = 0; kk < C::DK; ++kk) {
+            u32x4 w = row_ok ? *(const u32x4*)(qrow + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+            st.qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
+    st.m_run = neg_inf();
+    st.l_run = 0.f;
+    st.l_f32 = 0.f;
+
+    const int t_begin = lo_wg / C::BN;
+    const int t_end = hi_wg >= lo_wg ? hi_wg / C::BN : t_begin - 1;
+
+    uint32_t krc[C::KLW], vrc[C::VLW];
+    tile_rows_chunks<D, C::KS, C::KLOADS>(krc, wave, lane);
+    tile_rows_chunks<D, C::VS, C::VLOADS>(vrc, wave, lane);
+    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+
+    const int32_t* bt = pp.block_table + (size_t)seq * pp.max_pages;
+    const int last_page = max((L + 15) / 16 - 1, 0);
+    const size_t head_off = (size_t)hkv * 16 * D;
+    const size_t page_elems = (size_t)pp.Hkv * 16 * D;
+    // Block-table entries of a tile's four pages.  Indices past the
+    // sequence's last page are clamped to it (those rows read the zero row,
+    // so the entry is never used), which keeps every read inside the table.
+    struct Pages { int32_t e0, e1, e2, e3; };
+    auto entries = [&](int t) __attribute__((always_inline)) {
+        const int lp = t * (C::BN / 16);
+        Pages pg;
+        pg.e0 = bt[min(lp + 0, last_page)];
+        pg.e1 = bt[min(lp + 1, last_page)];
+        pg.e2 = bt[min(lp + 2, last_page)];
+        pg.e3 = bt[min(lp + 3, last_page)];
+        return pg;
+    };
+    auto copy_tile = [&](int t, const Pages& pg, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+        const size_t pb0 = (size_t)__builtin_amdgcn_readfirstlane(pg.e0) * page_elems + head_off;
+        const size_t pb1 = (size_t)__builtin_amdgcn_readfirstlane(pg.e1) * page_elems + head_off;
+        const size_t pb2 = (size_t)__builtin_amdgcn_readfirstlane(pg.e2) * page_elems + head_off;
+        const size_t pb3 = (size_t)__builtin_amdgcn_readfirstlane(pg.e3) * page_elems + head_off;
+        const int rows = L - t * C::BN;
+        load_paged_tile_async<D, C::KLOADS>(pp.k_pages, pb0, pb1, pb2, pb3, rows, kd, krc, wave);
+        load_paged_tile_async<D, C::VLOADS>(pp.v_pages, pb0, pb1, pb2, pb3, rows, vd, vrc, wave);
+    };
+
+    // Stage t: wait for tile t's copies (and tile t+1's block-table entries,
+    // read one stage ahead so their latency hides under a tile of compute),
+    // copy tile t+1, read tile t+2's entries, compute tile t.
+    Pages next;
+    auto stage = [&](int t, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
+        __syncthreads();
+        if (t < t_end) {
+            copy_tile(t + 1, next, kn, vn);
+            if (t + 1 < t_end) next = entries(t + 2);
+        }
+        const int n0 = t * C::BN;
+        const bool active = wave_has_rows && n0 <= hi_w_last && n0 + C::BN - 1 >= lo_w_first;
+        if (active) {
+            const bool full = n0 >= lo_w_last && n0 + C::BN - 1 <= hi_w_first;
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, pp.scale_log2, lane);
+        }
+    };
+
+    if (t_begin <= t_end) {
+        copy_tile(t_begin, entries(t_begin), k_lds0, v_lds0);
+        if (t_begin < t_end) next = entries(t_begin + 1);
+        for (int t = t_begin; t <= t_end; t += 2) {
+            stage(t, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (t + 1 <= t_end) stage(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
+    }
+    const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    if (row_ok) {
+        const bool any = l_tot > 0.f;
+        const float inv = any ? 1.f / l_tot : 0.f;
+        uint16_t* orow = pp.o + (size_t)(q0 + row) * row_stride + (size_t)hq * D;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 w;
+                w[0] = pack_bf16x2(st.acc[cb][4 * gq + 0] * inv, st.acc[cb][4 * gq + 1] * inv);
+                w[1] = pack_bf16x2(st.acc[cb][4 * gq + 2] * inv, st.acc[cb][4 * gq + 3] * inv);
+                *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
+            }
+        if (pp.lse != nullptr && lane < 32)
+            pp.lse[(size_t)(q0 + row) * pp.Hq + hq] = any ? (st.m_run + fast_log2(lf_tot)) * kLn2 : neg_inf();
+    }
+}
+
+int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t stream) {
+    const int blocks = p.num_seqs * p.Hq * p.num_q_tiles;
+    if (d == 128)
+        hipLaunchKernelGGL(paged_prefill_bf16_kernel<128>, dim3(blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(paged_prefill_bf16_kernel<64>, dim3(blocks), dim3(256), 0, stream, p);
+    return 0;
+}
+
 int prefill_bf16_rows_per_block() { return PrefillBf16Cfg<128>::BM; }
 
 int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {

@@ -147,6 +147,43 @@ int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                       int max_pages_per_seq, int max_seq_len, float scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attn_paged_prefill — chunked prefill over the paged KV cache: each
+ * sequence appends a chunk of new tokens and those tokens attend to the
+ * sequence's whole cache, read through its block table.  This is the serving
+ * pattern that pairs a tiled attention kernel with KV paging (the
+ * FlashAttention serving-value question page, Real-world examples; paged
+ * kernels on the "Attention and matrix kernels" page).
+ *
+ *   q            [total_q, Hq, d]                        bf16, read only;
+ *                token-major: row t is token t of the concatenated chunks
+ *   k_pages      [num_pages, Hkv, page_size, d]          bf16, read only
+ *   v_pages      [num_pages, Hkv, page_size, d]          bf16, read only
+ *   block_table  [num_seqs, max_pages_per_seq]           int32 (as for decode)
+ *   seq_lens     [num_seqs]                              int32: cached tokens of
+ *                each sequence, the chunk's own tokens included
+ *   q_offsets    [num_seqs + 1]                          int32, nondecreasing,
+ *                q_offsets[0] = 0: chunk s is rows q_offsets[s] .. q_offsets[s+1]-1
+ *   o            [total_q, Hq, d]                        bf16, written in full
+ *   lse          [total_q, Hq]                           float32 natural-log LSE; may be NULL
+ *
+ * Query i of chunk s (Nq_s = q_offsets[s+1] - q_offsets[s] tokens) stands at
+ * key position i + seq_lens[s] - Nq_s, the bottom-right alignment of the mask
+ * definitions above; mask NONE, CAUSAL or SLIDING_WINDOW applies within each
+ * sequence (DOCUMENT returns ATTN_ERR_UNSUPPORTED).  Page slots past seq_len
+ * are never read into the result (any bit pattern, NaN included).  Rows with
+ * no visible key (a chunk longer than its cache, seq_len = 0) get O = 0 and
+ * LSE = -inf.  Caller contract (not checked, like all device-resident index
+ * data): Nq_s <= max_q_len, seq_lens[s] <= max_seq_len <= max_pages_per_seq *
+ * page_size.  page_size must be 16, d 128 or 64, Hq a multiple of Hkv.
+ */
+int attn_paged_prefill(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_offsets,
+                       void* o, float* lse,
+                       int num_seqs, int Hq, int Hkv, int d, int page_size,
+                       int max_pages_per_seq, int max_seq_len, int max_q_len, float scale,
+                       attn_mask mask, hipStream_t stream);
+
 /* Text for a status code (static storage; for ATTN_ERR_HIP, thread-local). */
 const char* attn_status_string(int status);
 

@@ -19,9 +19,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_five_entry_points():
     assert declared_functions() == ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-                                    "attn_status_string"]
+                                    "attn_paged_prefill", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -91,3 +91,26 @@ def test_workspace_size():
     assert f(64, 32, 128, 32768) < 64 * 32 * 64 * 129 * 4 + 4096
     assert f(64, 32, 128, 1024) < f(64, 32, 128, 1025) <= f(64, 32, 128, 2048)
     assert f(1, 1, 96, 10) == 0 and f(-1, 1, 128, 10) == 0
+
+
+def chunked(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qo=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128,
+            page=16, max_pages=4, max_len=64, max_q=32, scale=0.1, kind=1, window=0):
+    m = _lib.AttnMask(kind, window, None, 0)
+    return _lib.lib().attn_paged_prefill(q, kp, vp, bt, sl, qo, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
+                                         max_q, scale, m, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=32), 2), (dict(d=96), 2), (dict(kind=3), 2), (dict(kind=7), 1), (dict(kind=2, window=0), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(max_pages=3), 1), (dict(S=-1), 1), (dict(max_q=-1), 1),
+    (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(q=None), 1), (dict(qo=None), 1),
+    (dict(sl=None), 1), (dict(bt=None), 1), (dict(kp=FAKE + 2), 1), (dict(o=FAKE + 8), 1),
+    (dict(max_len=1 << 29, max_pages=1 << 25), 2),
+])
+def test_paged_prefill_rejects_bad_arguments(kw, status):
+    assert chunked(**kw) == status
+
+
+def test_paged_prefill_empty_problems_are_noops():
+    assert chunked(q=None, kp=None, vp=None, bt=None, sl=None, qo=None, o=None, lse=None, S=0) == 0
+    assert chunked(q=None, kp=None, vp=None, bt=None, sl=None, qo=None, o=None, lse=None, max_q=0) == 0

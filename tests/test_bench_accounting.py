@@ -39,3 +39,13 @@ def test_decode_config_bytes():
     c = workloads.decode_config("c5_paged_decode_64", with_values=False)
     assert int(c["seq_lens"].sum()) == 1_101_299
     assert bench.decode_bytes(c) == 4_512_253_168
+
+
+def test_chunked_visible_pairs_closed_form():
+    # causal chunk of n queries at the end of L cached keys: query i sees
+    # L - n + i + 1 keys, so the chunk sees n (L - n) + n (n + 1) / 2 pairs
+    c = workloads.chunked_config("c6_chunked_prefill_16")
+    n = np.diff(c["q_offsets"]).astype(np.int64)
+    L = c["seq_lens"].astype(np.int64)
+    assert bench.chunked_visible_pairs(c) == int(np.sum(n * (L - n) + n * (n + 1) // 2))
+    assert bench.chunked_flops(c) == 4 * 128 * 32 * bench.chunked_visible_pairs(c)
