@@ -25,7 +25,11 @@ Readings of points the pages leave open (kept identical in the kernels):
     document masks, "Attention and matrix kernels" page, How it works);
   * grouped-query heads are contiguous groups: kv head = q head // (Hq / Hkv)
     (MQA and GQA section);
-  * a row that sees no key has output 0 and LSE -inf.
+  * a row that sees no key has output 0 and LSE -inf (LSE = the sink logit
+    when a learned per-head sink is given);
+  * sink tokens keep the first keys visible beside a sliding window, and a
+    learned per-head sink logit joins each row's softmax denominator with a
+    zero value (AIB, Sliding windows and local:global layers).
 
 Parity pins: see tests/test_oracle_pins.py (brute force in 50-digit
 arithmetic, closed forms, invariants, reductions and the worked example the
@@ -53,17 +57,21 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def visibility(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None,
-               rows: np.ndarray | None = None) -> np.ndarray:
+               rows: np.ndarray | None = None, sink_tokens: int = 0) -> np.ndarray:
     """Boolean matrix vis[i, j]: may query row i attend to key j?
 
     Query i stands at key position pos = i + (Nk - Nq).
       none      every key
       causal    j <= pos
-      window    0 <= pos - j < window
+      window    0 <= pos - j < window, or j < sink_tokens and j <= pos (the
+                first tokens kept visible beside the recent window, as
+                StreamingLLM does: AIB, Sliding windows and local:global layers)
       document  j <= pos and key j lies in the same document as position pos
     """
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
+    if sink_tokens and mask != "window":
+        raise ValueError("sink tokens apply to the window mask only")
     i = np.arange(Nq) if rows is None else np.asarray(rows)
     pos = (i + (Nk - Nq))[:, None]
     j = np.arange(Nk)[None, :]
@@ -74,7 +82,7 @@ def visibility(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None,
     if mask == "window":
         if window < 1:
             raise ValueError("window must be >= 1")
-        return (pos - j >= 0) & (pos - j < window)
+        return (pos - j >= 0) & ((pos - j < window) | (j < sink_tokens))
     off = np.asarray(doc_offsets, dtype=np.int64)
     # document id of a key position: the last offset that is <= the position
     doc_of_key = np.searchsorted(off, np.arange(Nk), side="right") - 1
@@ -85,13 +93,21 @@ def visibility(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None,
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: str = "none",
-              window: int = 0, doc_offsets=None, rows=None, row_block: int = 1024):
+              window: int = 0, doc_offsets=None, rows=None, row_block: int = 1024,
+              sink_tokens: int = 0, sink_logits=None):
     """O = softmax(scale·Q·Kᵀ + mask)·V and LSE, in float64.
 
     q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d] (float64).  Returns o with q's
     shape (or [B, Hq, len(rows), d] when ``rows`` selects query rows) and
     lse [B, Hq, Nq] (or [B, Hq, len(rows)]).  Rows are independent, so a row
     subset is exact for the rows it lists.
+
+    ``sink_logits`` [Hq] (optional): a learned sink per query head, as gpt-oss
+    has (AIB, Sliding windows and local:global layers): each row's softmax
+    runs over its visible scores plus one more entry whose logit is the
+    head's sink and whose value is zero.  It only enlarges the denominator:
+    O = Σ e^s v / (Σ e^s + e^sink), LSE = ln(Σ e^s + e^sink); a row with no
+    visible key gets O = 0 and LSE = sink.  ``sink_tokens``: see visibility.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -105,14 +121,17 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
     group = Hq // Hkv
     row_idx = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_idx.size
+    sinks = None if sink_logits is None else np.asarray(sink_logits, dtype=np.float64).reshape(Hq)
     o = np.zeros((B, Hq, R, d), dtype=np.float64)
     lse = np.full((B, Hq, R), -np.inf, dtype=np.float64)
+    if sinks is not None:
+        lse[:] = sinks[None, :, None]          # the rows that see no key keep LSE = sink
     if R == 0 or Nk == 0:
         return o, lse
     scale = float(scale)
     for r0 in range(0, R, row_block):
         sel = row_idx[r0:r0 + row_block]
-        vis = visibility(Nq, Nk, mask, window, doc_offsets, rows=sel)
+        vis = visibility(Nq, Nk, mask, window, doc_offsets, rows=sel, sink_tokens=sink_tokens)
         any_vis = vis.any(axis=1)
         for b in range(B):
             for h in range(Hq):
@@ -120,6 +139,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
                 # step 1: scores for the full rows, then the additive mask
                 s = scale * (q[b, h, sel, :] @ k[b, hk].T)
                 s = np.where(vis, s, -np.inf)
+                if sinks is not None:          # the sink joins each row as one more score
+                    s = np.concatenate([s, np.full((sel.size, 1), sinks[h])], axis=1)
                 # step 2: probabilities
                 m = np.max(s, axis=1, keepdims=True)
                 m = np.where(np.isfinite(m), m, 0.0)
@@ -127,10 +148,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
                 l = e.sum(axis=1, keepdims=True)
                 safe_l = np.where(l > 0, l, 1.0)
                 p = e / safe_l
-                # step 3: output and the log-sum-exp statistic
-                o[b, h, r0:r0 + sel.size] = p @ v[b, hk]
+                # step 3: output (the sink's value is zero) and the log-sum-exp statistic
+                o[b, h, r0:r0 + sel.size] = p[:, :Nk] @ v[b, hk]
                 lse_blk = m[:, 0] + np.log(safe_l[:, 0])
-                lse[b, h, r0:r0 + sel.size] = np.where(any_vis, lse_blk, -np.inf)
+                if sinks is None:
+                    lse[b, h, r0:r0 + sel.size] = np.where(any_vis, lse_blk, -np.inf)
+                else:
+                    lse[b, h, r0:r0 + sel.size] = lse_blk
         o[:, :, r0:r0 + sel.size][:, :, ~any_vis] = 0.0
     return o, lse
 
@@ -148,7 +172,7 @@ def gather_sequence(pages: np.ndarray, block_table_row: np.ndarray, seq_len: int
 
 
 def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
-                 seq_lens: np.ndarray, scale: float, seqs=None, dtype: str = "f64"):
+                 seq_lens: np.ndarray, scale: float, seqs=None, dtype: str = "f64", sink_logits=None):
     """One-token decode over a paged KV cache, in float64.
 
     q [S, Hq, d]; k_pages/v_pages [P, Hkv, page_size, d]; block_table
@@ -163,6 +187,8 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
     seqs = range(S) if seqs is None else list(seqs)
     out_o = np.zeros((len(seqs), Hq, d), dtype=np.float64)
     out_l = np.full((len(seqs), Hq), -np.inf, dtype=np.float64)
+    if sink_logits is not None:
+        out_l[:] = np.asarray(sink_logits, dtype=np.float64)[None, :]
     for n, s in enumerate(seqs):
         L = int(seq_lens[s])
         if L == 0:
@@ -173,7 +199,7 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
             ks, vs = from_bf16_bits(ks), from_bf16_bits(vs)
         else:
             ks, vs = ks.astype(np.float64), vs.astype(np.float64)
-        o, lse = attention(q[s][None, :, None, :], ks[None], vs[None], scale, "none")
+        o, lse = attention(q[s][None, :, None, :], ks[None], vs[None], scale, "none", sink_logits=sink_logits)
         out_o[n] = o[0, :, 0, :]
         out_l[n] = lse[0, :, 0]
     return out_o, out_l
@@ -181,7 +207,7 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
 
 def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
                   seq_lens: np.ndarray, q_offsets: np.ndarray, scale: float, mask: str = "causal",
-                  window: int = 0, seqs=None, dtype: str = "f64"):
+                  window: int = 0, seqs=None, dtype: str = "f64", sink_tokens: int = 0, sink_logits=None):
     """Chunked prefill over a paged KV cache, in float64.
 
     The serving pattern that pairs a tiled attention kernel with KV paging
@@ -210,6 +236,8 @@ def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block
         n, L = b - a, int(seq_lens[s])
         o = np.zeros((n, Hq, d), dtype=np.float64)
         lse = np.full((n, Hq), -np.inf, dtype=np.float64)
+        if sink_logits is not None:
+            lse[:] = np.asarray(sink_logits, dtype=np.float64)[None, :]
         if n > 0 and L > 0:
             ks = gather_sequence(k_pages, block_table[s], L)
             vs = gather_sequence(v_pages, block_table[s], L)
@@ -218,7 +246,8 @@ def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block
             else:
                 ks, vs = ks.astype(np.float64), vs.astype(np.float64)
             qs = np.transpose(q[a:b], (1, 0, 2))[None]          # [1, Hq, n, d]
-            os_, ls_ = attention(qs, ks[None], vs[None], scale, mask, window)
+            os_, ls_ = attention(qs, ks[None], vs[None], scale, mask, window, sink_tokens=sink_tokens,
+                                 sink_logits=sink_logits)
             o = np.transpose(os_[0], (1, 0, 2))
             lse = np.transpose(ls_[0], (1, 0))
         outs_o.append(o)

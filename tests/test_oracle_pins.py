@@ -459,3 +459,97 @@ def test_generated_chunked_layout_is_nan_safe():
                                   c["q_offsets"], c["scale"], "causal", dtype="bf16")
     assert o.shape == (int(c["q_offsets"][-1]), 4, 16)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ------------------------------------------------------------------- sinks
+
+def _brute_sinks(q, k, v, scale, mask, window, sink_tokens, sinks):
+    """50-digit reference: visible keys by rule (window plus the first sink_tokens
+    keys, causally), and a per-head sink term e^sink in every denominator."""
+    mpmath.mp.dps = 50
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros(q.shape)
+    L = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            for i in range(Nq):
+                pos = i + Nk - Nq
+                keys = _visible_keys(i, Nq, Nk, mask, window, None)
+                if mask == "window":
+                    keys = sorted(set(keys) | {j for j in range(min(sink_tokens, Nk)) if j <= pos})
+                w = {j: mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, h, i, c]) * mpmath.mpf(k[b, hk, j, c])
+                                                                   for c in range(d))) for j in keys}
+                tot = mpmath.fsum(w.values())
+                if sinks is not None:
+                    tot += mpmath.exp(mpmath.mpf(sinks[h]))
+                if tot == 0:
+                    continue
+                for c in range(d):
+                    O[b, h, i, c] = float(mpmath.fsum(w[j] * mpmath.mpf(v[b, hk, j, c]) for j in keys) / tot)
+                L[b, h, i] = float(mpmath.log(tot))
+    return O, L
+
+
+@pytest.mark.parametrize("mask,window,sink_tokens,with_logits", [
+    ("window", 2, 2, False), ("window", 3, 1, True), ("window", 2, 9, False),
+    ("causal", 0, 0, True), ("none", 0, 0, True), ("window", 1, 0, True),
+])
+def test_sinks_brute_force_tiny(mask, window, sink_tokens, with_logits):
+    B, Hq, Hkv, d, Nq, Nk = 1, 4, 2, 3, 7, 8
+    q, k, v = rnd(71, B, Hq, Nq, d), rnd(72, B, Hkv, Nk, d), rnd(73, B, Hkv, Nk, d)
+    sinks = np.array([0.3, -1.2, 2.5, -40.0]) if with_logits else None
+    o, lse = oracle.attention(q, k, v, 0.8, mask, window, sink_tokens=sink_tokens, sink_logits=sinks)
+    ob, lb = _brute_sinks(q, k, v, 0.8, mask, window, sink_tokens, sinks)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-13)
+
+
+def test_sink_logit_is_one_more_denominator_term():
+    # with sink σ: LSE' = logaddexp(LSE, σ) and O' = O · exp(LSE − LSE'); rows
+    # that see nothing get O = 0, LSE = σ
+    q, k, v = rnd(81, 1, 4, 9, 8), rnd(82, 1, 2, 6, 8), rnd(83, 1, 2, 6, 8)
+    sinks = np.array([-3.0, 0.0, 1.5, 6.0])
+    o, lse = oracle.attention(q, k, v, 0.5, "causal")          # Nq > Nk: rows 0..2 see nothing
+    os_, ls_ = oracle.attention(q, k, v, 0.5, "causal", sink_logits=sinks)
+    want_l = np.logaddexp(lse, sinks[None, :, None])
+    np.testing.assert_allclose(ls_, want_l, rtol=0, atol=1e-13)
+    fin = np.isfinite(lse)
+    scale_o = np.where(fin, np.exp(np.where(fin, lse, 0.0) - want_l), 0.0)
+    np.testing.assert_allclose(os_, o * scale_o[..., None], rtol=0, atol=1e-13)
+    assert np.all(os_[~fin] == 0.0) and np.allclose(ls_[~fin], np.broadcast_to(sinks[None, :, None], ls_.shape)[~fin])
+
+
+def test_sink_reductions():
+    q, k, v = rnd(91, 1, 2, 12, 4), rnd(92, 1, 2, 12, 4), rnd(93, 1, 2, 12, 4)
+    base = oracle.attention(q, k, v, 0.9, "window", 3)
+    # no sink tokens = the plain window; a -inf sink logit = no sink
+    for got in (oracle.attention(q, k, v, 0.9, "window", 3, sink_tokens=0),
+                oracle.attention(q, k, v, 0.9, "window", 3, sink_logits=np.full(2, -np.inf))):
+        np.testing.assert_array_equal(got[0], base[0])
+        np.testing.assert_array_equal(got[1], base[1])
+    # sink tokens covering every key = causal
+    c = oracle.attention(q, k, v, 0.9, "causal")
+    w = oracle.attention(q, k, v, 0.9, "window", 3, sink_tokens=12)
+    np.testing.assert_allclose(w[0], c[0], atol=1e-15)
+    np.testing.assert_allclose(w[1], c[1], atol=1e-15)
+    # and a visibility check of the rule itself: key 0 stays visible from every row
+    vis = oracle.visibility(12, 12, "window", 3, sink_tokens=1)
+    assert vis[:, 0].all() and vis.sum() == sum(min(3, i + 1) + (1 if i >= 3 else 0) for i in range(12))
+    with pytest.raises(ValueError):
+        oracle.visibility(4, 4, "causal", sink_tokens=1)
+
+
+def test_paged_paths_carry_the_sink():
+    c = workloads.make_decode(3, 4, 2, 8, len_min=0, len_max=40, seq_lens=[0, 17, 33], max_seq_len=40, seed=9,
+                              tail_fill="nan")
+    sinks = np.array([0.5, -1.0, 2.0, 0.0])
+    o, lse = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"], c["scale"],
+                                 dtype="bf16", sink_logits=sinks)
+    assert np.all(o[0] == 0.0) and np.array_equal(lse[0], sinks)          # empty cache: LSE = sink
+    op, lp = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                  np.arange(4), c["scale"], "causal", dtype="bf16", sink_logits=sinks)
+    np.testing.assert_array_equal(op, o)
+    np.testing.assert_array_equal(lp, lse)
