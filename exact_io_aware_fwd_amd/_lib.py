@@ -24,7 +24,8 @@ MASK_KINDS = {"none": 0, "causal": 1, "window": 2, "document": 3}
 
 class AttnMask(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("doc_offsets", ctypes.c_void_p), ("num_docs", ctypes.c_int32)]
+                ("doc_offsets", ctypes.c_void_p), ("num_docs", ctypes.c_int32),
+                ("sink_tokens", ctypes.c_int32), ("sink_logits", ctypes.c_void_p)]
 
 
 _lib = None
@@ -43,7 +44,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_paged_decode_workspace_size.argtypes = [i, i, i, i]
     L.attn_paged_decode_workspace_size.restype = sz
-    L.attn_paged_decode.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, p, sz, p]
+    L.attn_paged_decode.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, p, p, sz, p]
     L.attn_paged_decode.restype = i
     L.attn_paged_prefill.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, AttnMask, p]
     L.attn_paged_prefill.restype = i

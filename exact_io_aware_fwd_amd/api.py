@@ -30,11 +30,22 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
-def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None) -> _lib.AttnMask:
+def _sink_ptr(sink_logits: torch.Tensor | None, Hq: int):
+    if sink_logits is None:
+        return None
+    _need(sink_logits.dtype == torch.float32 and sink_logits.is_cuda and sink_logits.is_contiguous()
+          and sink_logits.numel() == Hq, "sink_logits must be a contiguous float32 device tensor of Hq entries")
+    return sink_logits.data_ptr()
+
+
+def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
+              sink_tokens: int = 0, sink_logits: torch.Tensor | None = None, Hq: int = 0) -> _lib.AttnMask:
     _need(mask in _lib.MASK_KINDS, f"unknown mask {mask!r}")
     m = _lib.AttnMask()
     m.kind = _lib.MASK_KINDS[mask]
     m.window = int(window) if mask == "window" else 0
+    m.sink_tokens = int(sink_tokens)
+    m.sink_logits = _sink_ptr(sink_logits, Hq)
     if mask == "document":
         _need(doc_offsets is not None and doc_offsets.dtype == torch.int32 and doc_offsets.is_cuda
               and doc_offsets.is_contiguous(), "document mask needs int32 device doc_offsets")
@@ -48,9 +59,11 @@ def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | N
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float | None = None,
              mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
+             sink_tokens: int = 0, sink_logits: torch.Tensor | None = None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None, with_lse: bool = True,
              stream=None):
-    """Attention forward: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> (o [B,Hq,Nq,d], lse [B,Hq,Nq] fp32)."""
+    """Attention forward: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> (o [B,Hq,Nq,d], lse [B,Hq,Nq] fp32).
+    sink_tokens (window mask) and sink_logits [Hq] fp32 are the optional attention sinks."""
     _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-d [B, H, N, d]")
     _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "dtype must be bf16 or fp32, same for q/k/v")
     _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous device tensors")
@@ -63,7 +76,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    m = make_mask(mask, window, doc_offsets)
+    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq)
     st = _lib.lib().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                              None if lse is None else ctypes_ptr(lse),
                              B, Hq, Hkv, Nq, Nk, d, float(scale), m, _DTYPES[q.dtype], _stream(stream))
@@ -77,7 +90,8 @@ def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, d: int, max_seq_len
 
 def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                       block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
-                      scale: float | None = None, workspace: torch.Tensor | None = None,
+                      scale: float | None = None, sink_logits: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None,
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       with_lse: bool = True, stream=None):
     """Paged decode: q [S,Hq,d], pages [P,Hkv,16,d] -> (o [S,Hq,d] bf16, lse [S,Hq] fp32)."""
@@ -103,7 +117,8 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                       ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(out),
                                       None if lse is None else ctypes_ptr(lse),
                                       S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
-                                      float(scale), ctypes_ptr(workspace), workspace.numel(), _stream(stream))
+                                      float(scale), _sink_ptr(sink_logits, Hq), ctypes_ptr(workspace),
+                                      workspace.numel(), _stream(stream))
     _lib.check(st)
     return out, lse
 
@@ -111,7 +126,8 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
 def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                        block_table: torch.Tensor, seq_lens: torch.Tensor, q_offsets: torch.Tensor, *,
                        max_seq_len: int, max_q_len: int, scale: float | None = None, mask: str = "causal",
-                       window: int = 0, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       window: int = 0, sink_tokens: int = 0, sink_logits: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                        with_lse: bool = True, stream=None):
     """Chunked prefill over the paged cache: q [T,Hq,d] token-major, pages [P,Hkv,16,d],
     q_offsets [S+1] -> (o [T,Hq,d] bf16, lse [T,Hq] fp32)."""
@@ -132,7 +148,7 @@ def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    m = make_mask(mask, window)
+    m = make_mask(mask, window, None, sink_tokens, sink_logits, Hq)
     st = _lib.lib().attn_paged_prefill(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
                                        ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(q_offsets),
                                        ctypes_ptr(out), None if lse is None else ctypes_ptr(lse),

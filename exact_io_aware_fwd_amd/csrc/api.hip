@@ -29,6 +29,13 @@ int hip_status(hipError_t e) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// sink tokens: window mask only, >= 0; sink logits: any kind, 4-byte aligned
+bool sinks_ok(const attn_mask& m) {
+    if (m.sink_tokens < 0) return false;
+    if (m.sink_tokens > 0 && m.kind != ATTN_MASK_SLIDING_WINDOW) return false;
+    return ((uintptr_t)m.sink_logits & 3u) == 0;
+}
+
 }  // namespace
 
 extern "C" const char* attn_status_string(int status) {
@@ -51,6 +58,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_DOCUMENT && (mask.num_docs < 1 || mask.doc_offsets == nullptr))
         return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
@@ -73,6 +81,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.doc_offsets = mask.kind == ATTN_MASK_DOCUMENT ? mask.doc_offsets : nullptr;
     p.num_docs = mask.kind == ATTN_MASK_DOCUMENT ? mask.num_docs : 0;
     p.num_q_tiles = (int)tiles;
+    p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
+    p.sink_logits = mask.sink_logits;
 
     if (dtype == ATTN_DTYPE_BF16)
         xattn::launch_prefill_bf16(p, d, stream);
@@ -90,12 +100,13 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  void* o, float* lse,
                                  int num_seqs, int Hq, int Hkv, int d, int page_size,
-                                 int max_pages_per_seq, int max_seq_len, float scale,
+                                 int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (num_seqs < 0 || Hq < 0 || Hkv < 0 || d < 0 || max_pages_per_seq < 0 || max_seq_len < 0)
         return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)sink_logits & 3u) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
     if ((long long)max_pages_per_seq * page_size < max_seq_len) return ATTN_ERR_INVALID_ARGUMENT;
@@ -119,6 +130,7 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
     p.num_seqs = num_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
     p.max_pages = max_pages_per_seq; p.max_splits = 0;
     p.scale_log2 = scale * xattn::kLog2e;
+    p.sink_logits = sink_logits;
     p.ws_o = nullptr; p.ws_lse = nullptr;
     xattn::launch_decode(p, d, max_seq_len, workspace, stream);
     return hip_status(hipGetLastError());
@@ -136,6 +148,7 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind < ATTN_MASK_NONE || mask.kind > ATTN_MASK_DOCUMENT) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_DOCUMENT) return ATTN_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
@@ -162,6 +175,8 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     p.scale_log2 = scale * xattn::kLog2e;
     p.mask_kind = mask.kind;
     p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.window : 0;
+    p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
+    p.sink_logits = mask.sink_logits;
     xattn::launch_paged_prefill_bf16(p, d, stream);
     return hip_status(hipGetLastError());
 }

@@ -36,6 +36,8 @@ struct PrefillParams {
     const int32_t* doc_offsets;
     int num_docs;
     int num_q_tiles;
+    int sink_end;              // window mask: keys [0, sink_end) stay visible too (0: none)
+    const float* sink_logits;  // [Hq] learned sink logit per query head, or null
 };
 
 // Arguments of one chunked-prefill launch over the paged cache (validated on
@@ -55,6 +57,8 @@ struct PagedPrefillParams {
     float scale_log2;
     int mask_kind;              // none, causal or window
     int window;
+    int sink_end;               // window mask: keys [0, sink_end) stay visible too
+    const float* sink_logits;   // [Hq] or null
 };
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
@@ -90,6 +94,57 @@ __device__ __forceinline__ void row_interval(const PrefillParams& p, int i, int&
     } else {
         lo = doc_start(p.doc_offsets, p.num_docs, pos);
     }
+}
+
+// Sink tokens (StreamingLLM's, "Attention Is the Bottleneck", Sliding windows
+// and local:global layers) add a second visible interval [0, sink_end) to a
+// window row's [lo, hi] (causality still applies: only keys <= hi).  A
+// workgroup then visits the sink tiles [0, s0) first and its window tiles
+// after them; iteration it runs tile tile_of(it).  When the sink tiles reach
+// the window tiles the union is one range starting at tile 0.
+struct TileRange {
+    int s0;        // sink tiles visited before the window range
+    int t_begin;   // first tile of the window range
+    int n;         // iterations
+};
+
+__device__ __forceinline__ TileRange tile_range(int lo_wg, int hi_wg, int sink_end, int bn) {
+    TileRange r;
+    int t_begin = lo_wg / bn;
+    const int t_end = hi_wg >= lo_wg ? hi_wg / bn : t_begin - 1;
+    int s0 = 0;
+    if (t_end >= t_begin && sink_end > 0) {
+        const int sk = min((sink_end + bn - 1) / bn, t_end + 1);
+        if (sk >= t_begin) t_begin = 0;
+        else s0 = sk;
+    }
+    r.s0 = s0;
+    r.t_begin = t_begin;
+    r.n = t_end >= t_begin ? s0 + t_end - t_begin + 1 : 0;
+    return r;
+}
+
+__device__ __forceinline__ int tile_of(const TileRange& r, int it) { return it < r.s0 ? it : r.t_begin + it - r.s0; }
+
+// Row statistics to output scale and LSE, folding in an optional learned
+// sink (base-2 logit s2, -inf for none) as one more denominator term with a
+// zero value (gpt-oss's per-head sink, same page and section):
+//   O = acc * a / (l_o * a + b),  LSE = ln 2 * (M + log2(l_lse * a + b))
+// with M = max(m_run, s2), a = 2^(m_run - M), b = 2^(s2 - M), so nothing
+// overflows whichever term dominates.  Without a sink this is acc / l_o and
+// m_run + log2(l_lse); a row that saw no key and has no sink gets 0 / -inf.
+__device__ __forceinline__ void finish_row(float m_run, float l_o, float l_lse, float s2, float& inv, float& lse) {
+    const float M = fmaxf(m_run, s2);
+    if (M == -__builtin_inff()) {
+        inv = 0.f;
+        lse = -__builtin_inff();
+        return;
+    }
+    const float a = __builtin_amdgcn_exp2f(m_run - M);
+    const float b = __builtin_amdgcn_exp2f(s2 - M);
+    const float den = l_o * a + b;
+    inv = den > 0.f ? a / den : 0.f;
+    lse = (M + __builtin_amdgcn_logf(l_lse * a + b)) * kLn2;
 }
 
 // Workgroup id -> (b*Hkv + kv head, q tile, head within the group).

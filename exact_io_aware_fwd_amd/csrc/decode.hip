@@ -316,16 +316,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int len = p.seq_lens[s];
     const int ns = (len + kSplitTokens - 1) / kSplitTokens;
     uint16_t* orow = p.o + (size_t)pair * D;
+    // a learned per-head sink joins the merge as one more split with a zero
+    // partial output (base-2 logit s2; -inf when there is none)
+    const float s2 = p.sink_logits != nullptr ? p.sink_logits[pair % p.Hq] * kLog2e : neg_inf();
     if (ns <= 0) {
         for (int c = lane; c < D; c += 64) orow[c] = 0;
-        if (p.lse != nullptr && lane == 0) p.lse[pair] = neg_inf();
+        if (p.lse != nullptr && lane == 0) p.lse[pair] = p.sink_logits != nullptr ? p.sink_logits[pair % p.Hq] : neg_inf();
         return;
     }
     const float* wl = p.ws_lse + (size_t)pair * p.max_splits;
     const float* wo = p.ws_o + (size_t)pair * p.max_splits * D;
     float mx = neg_inf();
     for (int i = lane; i < ns; i += 64) mx = fmaxf(mx, wl[i]);
-    mx = wave_max(mx);
+    mx = fmaxf(wave_max(mx), s2);
     float acc[CPL] = {};
     float den = 0.f;
     for (int i0 = 0; i0 < ns; i0 += 64) {
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
             for (int e = 0; e < CPL; ++e) acc[e] = __builtin_fmaf(w, wo[(size_t)(i0 + i) * D + lane * CPL + e], acc[e]);
         }
     }
+    den += fast_exp2(s2 - mx);
     const float inv = 1.f / den;
     if (CPL == 2) {
         *(uint32_t*)(orow + lane * 2) = pack_bf16x2(acc[0] * inv, acc[CPL - 1] * inv);

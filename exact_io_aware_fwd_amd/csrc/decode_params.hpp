@@ -22,6 +22,7 @@ struct DecodeParams {
     float* ws_lse;   // [num_seqs, Hq, max_splits], base-2 log-sum-exp
     int num_seqs, Hq, Hkv, group, max_pages, max_splits;
     float scale_log2;
+    const float* sink_logits;   // [Hq] learned sink logit per query head, or null
 };
 
 size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len);

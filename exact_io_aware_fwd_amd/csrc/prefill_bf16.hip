@@ -107,7 +107,7 @@ struct PrefillBf16State {
 // K / V tile; every other operand address is a compile-time offset from it.
 template <int D>
 __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t* kl, const uint8_t* vl, int n0,
-                                          bool full, int lo_i, int hi_i, float scale_log2, int lane) {
+                                          bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane) {
     using C = PrefillBf16Cfg<D>;
     // ---- S^T = K Q^T, two 32-key blocks
     f32x16 s[2];
@@ -127,7 +127,7 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (key < lo_i || key > hi_i) s[jb][r] = neg_inf();
+                if (key > hi_i || (key < lo_i && key >= sink_end)) s[jb][r] = neg_inf();
             }
     }
     // Row max: each lane reduces its own half of the row (two independent
@@ -257,8 +257,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     st.l_run = 0.f;
     st.l_f32 = 0.f;
 
-    const int t_begin = lo_wg / C::BN;
-    const int t_end = hi_wg >= lo_wg ? hi_wg / C::BN : t_begin - 1;
+    const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, C::BN);
 
     uint32_t koff[C::KLW], voff[C::VLW];
     tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
@@ -270,38 +269,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     // One stage of the ring: wait for this tile's copies, make them visible to
     // every wave (which also proves every wave is done with the other stage),
     // start copying the next tile into the other stage, then compute.
-    auto stage = [&](int t, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+    // Iteration it runs tile tile_of(tr, it).
+    auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
         __syncthreads();
-        if (t < t_end) {
-            load_tile_async<D, C::KS, C::KLOADS>(kg_, (t + 1) * C::BN, p.Nk, kn, koff, wave);
-            load_tile_async<D, C::VS, C::VLOADS>(vg_, (t + 1) * C::BN, p.Nk, vn, voff, wave);
+        if (it + 1 < tr.n) {
+            const int tn = tile_of(tr, it + 1);
+            load_tile_async<D, C::KS, C::KLOADS>(kg_, tn * C::BN, p.Nk, kn, koff, wave);
+            load_tile_async<D, C::VS, C::VLOADS>(vg_, tn * C::BN, p.Nk, vn, voff, wave);
         }
-        const int n0 = t * C::BN;
-        const bool active = wave_has_rows && n0 <= hi_w_last && n0 + C::BN - 1 >= lo_w_first;
+        const int n0 = tile_of(tr, it) * C::BN;
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < p.sink_end);
         if (active) {
-            const bool full = n0 >= lo_w_last && n0 + C::BN - 1 <= hi_w_first;
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, p.scale_log2, lane);
+            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < p.sink_end);
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, p.sink_end, p.scale_log2, lane);
         }
     };
 
-    if (t_begin <= t_end) {
-        load_tile_async<D, C::KS, C::KLOADS>(kg_, t_begin * C::BN, p.Nk, k_lds0, koff, wave);
-        load_tile_async<D, C::VS, C::VLOADS>(vg_, t_begin * C::BN, p.Nk, v_lds0, voff, wave);
-        for (int t = t_begin; t <= t_end; t += 2) {
-            stage(t, k_lds0, v_lds0, k_lds1, v_lds1);
-            if (t + 1 <= t_end) stage(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    if (tr.n > 0) {
+        const int t0 = tile_of(tr, 0);
+        load_tile_async<D, C::KS, C::KLOADS>(kg_, t0 * C::BN, p.Nk, k_lds0, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(vg_, t0 * C::BN, p.Nk, v_lds0, voff, wave);
+        for (int it = 0; it < tr.n; it += 2) {
+            stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     }
     f32x16* acc = st.acc;
-    const float m_run = st.m_run, l_run = st.l_run;
     const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
 
-    // ---- epilogue: O = acc / l once, LSE in natural log
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // ---- epilogue: O = acc / l once, LSE in natural log (with the sink, if any)
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (row_ok) {
-        const bool any = l_tot > 0.f;
-        const float inv = any ? 1.f / l_tot : 0.f;
+        const float s2 = p.sink_logits != nullptr ? p.sink_logits[hq] * kLog2e : neg_inf();
+        float inv, lse_row;
+        finish_row(st.m_run, l_tot, lf_tot, s2, inv, lse_row);
         uint16_t* orow = (uint16_t*)p.o + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + row) * D;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
@@ -312,10 +314,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
                 w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
                 *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
             }
-        if (p.lse != nullptr && lane < 32) {
-            p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] =
-                any ? (m_run + fast_log2(lf_tot)) * kLn2 : neg_inf();
-        }
+        if (p.lse != nullptr && lane < 32) p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = lse_row;
     }
 }
 
@@ -391,6 +390,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     p.window = pp.window;
     p.doc_offsets = nullptr;
     p.num_docs = 0;
+    p.sink_end = pp.sink_end;
 
     const int r_last = min(r0 + C::BM, nq) - 1;
     const int w0 = r0 + wave * 32;
@@ -424,8 +424,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     st.l_run = 0.f;
     st.l_f32 = 0.f;
 
-    const int t_begin = lo_wg / C::BN;
-    const int t_end = hi_wg >= lo_wg ? hi_wg / C::BN : t_begin - 1;
+    const TileRange tr = tile_range(lo_wg, hi_wg, pp.sink_end, C::BN);
 
     uint32_t krc[C::KLW], vrc[C::VLW];
     tile_rows_chunks<D, C::KS, C::KLOADS>(krc, wave, lane);
@@ -460,38 +459,40 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
         load_paged_tile_async<D, C::VLOADS>(pp.v_pages, pb0, pb1, pb2, pb3, rows, vd, vrc, wave);
     };
 
-    // Stage t: wait for tile t's copies (and tile t+1's block-table entries,
-    // read one stage ahead so their latency hides under a tile of compute),
-    // copy tile t+1, read tile t+2's entries, compute tile t.
+    // Stage it: wait for its tile's copies (and the next tile's block-table
+    // entries, read one stage ahead so their latency hides under a tile of
+    // compute), copy the next tile, read the entries of the one after, compute.
     Pages next;
-    auto stage = [&](int t, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
+    auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of this tile landed
         __syncthreads();
-        if (t < t_end) {
-            copy_tile(t + 1, next, kn, vn);
-            if (t + 1 < t_end) next = entries(t + 2);
+        if (it + 1 < tr.n) {
+            copy_tile(tile_of(tr, it + 1), next, kn, vn);
+            if (it + 2 < tr.n) next = entries(tile_of(tr, it + 2));
         }
-        const int n0 = t * C::BN;
-        const bool active = wave_has_rows && n0 <= hi_w_last && n0 + C::BN - 1 >= lo_w_first;
+        const int n0 = tile_of(tr, it) * C::BN;
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < pp.sink_end);
         if (active) {
-            const bool full = n0 >= lo_w_last && n0 + C::BN - 1 <= hi_w_first;
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, pp.scale_log2, lane);
+            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < pp.sink_end);
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, pp.sink_end, pp.scale_log2, lane);
         }
     };
 
-    if (t_begin <= t_end) {
-        copy_tile(t_begin, entries(t_begin), k_lds0, v_lds0);
-        if (t_begin < t_end) next = entries(t_begin + 1);
-        for (int t = t_begin; t <= t_end; t += 2) {
-            stage(t, k_lds0, v_lds0, k_lds1, v_lds1);
-            if (t + 1 <= t_end) stage(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    if (tr.n > 0) {
+        const int t0 = tile_of(tr, 0);
+        copy_tile(t0, entries(t0), k_lds0, v_lds0);
+        if (tr.n > 1) next = entries(tile_of(tr, 1));
+        for (int it = 0; it < tr.n; it += 2) {
+            stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     }
     const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (row_ok) {
-        const bool any = l_tot > 0.f;
-        const float inv = any ? 1.f / l_tot : 0.f;
+        const float s2 = pp.sink_logits != nullptr ? pp.sink_logits[hq] * kLog2e : neg_inf();
+        float inv, lse_row;
+        finish_row(st.m_run, l_tot, lf_tot, s2, inv, lse_row);
         uint16_t* orow = pp.o + (size_t)(q0 + row) * row_stride + (size_t)hq * D;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
                 *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
             }
         if (pp.lse != nullptr && lane < 32)
-            pp.lse[(size_t)(q0 + row) * pp.Hq + hq] = any ? (st.m_run + fast_log2(lf_tot)) * kLn2 : neg_inf();
+            pp.lse[(size_t)(q0 + row) * pp.Hq + hq] = lse_row;
     }
 }
 

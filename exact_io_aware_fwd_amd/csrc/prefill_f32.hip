@@ -55,10 +55,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
     for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
     float m_run = neg_inf(), l_run = 0.f;
 
-    const int t_begin = lo_wg / BN;
-    const int t_end = hi_wg >= lo_wg ? hi_wg / BN : t_begin - 1;
-    for (int t = t_begin; t <= t_end; ++t) {
-        const int n0 = t * BN;
+    const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, BN);
+    for (int it = 0; it < tr.n; ++it) {
+        const int n0 = tile_of(tr, it) * BN;
         __syncthreads();  // previous tile fully consumed
         for (int c = tid; c < BN * D / 4; c += 256) {
             const int r = c / (D / 4), c4 = c % (D / 4);
@@ -70,18 +69,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
             *(f32x4*)(&v_lds[r * D + c4 * 4]) = vv;
         }
         __syncthreads();
-        const bool active = wave_has_rows && n0 <= hi_w_last && n0 + BN - 1 >= lo_w_first;
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + BN - 1 >= lo_w_first || n0 < p.sink_end);
         if (!active) continue;
         f32x16 s = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_lds[(lane & 31) * KSTR + kk * 2 + (lane >> 5)], qf[kk], s, 0, 0, 0);
-        const bool full = n0 >= lo_w_last && n0 + BN - 1 <= hi_w_first;
+        const bool full = n0 + BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + BN - 1 < p.sink_end);
         if (!full) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (key < lo_i || key > hi_i) s[r] = neg_inf();
+                if (key > hi_i || (key < lo_i && key >= p.sink_end)) s[r] = neg_inf();
             }
         }
         float mt = neg_inf();
@@ -113,8 +112,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (row_ok) {
-        const bool any = l_tot > 0.f;
-        const float inv = any ? 1.f / l_tot : 0.f;
+        const float s2 = p.sink_logits != nullptr ? p.sink_logits[hq] * kLog2e : neg_inf();
+        float inv, lse_row;
+        finish_row(m_run, l_tot, l_tot, s2, inv, lse_row);
         float* orow = (float*)p.o + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + row) * D;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
                 *(f32x4*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
             }
         if (p.lse != nullptr && lane < 32)
-            p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = any ? (m_run + fast_log2(l_tot)) * kLn2 : neg_inf();
+            p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = lse_row;
     }
 }
 

@@ -66,6 +66,19 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  *                   positions [doc_offsets[t], doc_offsets[t+1]).  The same
  *                   offsets apply to every batch element.
  * A query row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Sinks ("Attention Is the Bottleneck", Sliding windows and local:global
+ * layers), two optional extensions:
+ *   sink_tokens     SLIDING_WINDOW only (0 elsewhere): keys 0 .. sink_tokens-1
+ *                   stay visible to every query at or past them, besides the
+ *                   window (StreamingLLM's sink tokens).  >= 0.
+ *   sink_logits     NULL, or a DEVICE float32 array of Hq entries, 4-byte
+ *                   aligned: a learned sink per query head (as in gpt-oss).
+ *                   Each row's softmax gets one more entry with that logit
+ *                   (on the scale of scale * q.k, natural units) and a zero
+ *                   value: O = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink}),
+ *                   LSE = ln(sum_j e^{s_j} + e^{sink}); a row that sees no key
+ *                   gets O = 0 and LSE = sink.
  */
 typedef enum {
     ATTN_MASK_NONE = 0,
@@ -79,6 +92,8 @@ typedef struct {
     int32_t window;             /* SLIDING_WINDOW only: W >= 1 */
     const int32_t* doc_offsets; /* DOCUMENT only: device pointer, num_docs + 1 entries */
     int32_t num_docs;           /* DOCUMENT only: >= 1 */
+    int32_t sink_tokens;        /* SLIDING_WINDOW only: sink tokens kept visible, >= 0 */
+    const float* sink_logits;   /* NULL or device [Hq]: learned sink logit per query head */
 } attn_mask;
 
 /*
@@ -129,6 +144,8 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, int max_seq
  *   seq_lens     [num_seqs]                              int32, 0 <= len <= max_seq_len
  *   o            [num_seqs, Hq, d]                       bf16, written in full
  *   lse          [num_seqs, Hq]                          float32 natural-log LSE; may be NULL
+ *   sink_logits  NULL or device float32 [Hq]: learned sink per query head
+ *                (see the sinks paragraph above the mask struct)
  *   workspace    device scratch of at least
  *                attn_paged_decode_workspace_size(num_seqs, Hq, d, max_seq_len)
  *                bytes, 16-byte aligned; its contents on entry do not matter.
@@ -144,7 +161,7 @@ int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, const int32_t* seq_lens,
                       void* o, float* lse,
                       int num_seqs, int Hq, int Hkv, int d, int page_size,
-                      int max_pages_per_seq, int max_seq_len, float scale,
+                      int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -39,8 +39,8 @@ def test_status_strings():
 
 
 def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.1,
-        kind=0, window=0, doc=None, num_docs=0, dtype=1):
-    m = _lib.AttnMask(kind, window, doc, num_docs)
+        kind=0, window=0, doc=None, num_docs=0, dtype=1, sink_tokens=0, sinks=None):
+    m = _lib.AttnMask(kind, window, doc, num_docs, sink_tokens, sinks)
     return _lib.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype, None)
 
 
@@ -52,6 +52,8 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16
     (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
     (dict(q=None), 1), (dict(o=None), 1), (dict(k=None), 1), (dict(q=FAKE + 4), 1), (dict(v=FAKE + 8), 1),
     (dict(Nq=1 << 29), 2),
+    (dict(kind=1, sink_tokens=4), 1), (dict(kind=0, sink_tokens=1), 1), (dict(kind=2, window=8, sink_tokens=-1), 1),
+    (dict(sinks=FAKE + 2), 1), (dict(kind=2, window=8, sink_tokens=4, d=96), 2),
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
@@ -65,17 +67,17 @@ def test_fwd_empty_problems_are_noops():
 
 
 def dec(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128, page=16,
-        max_pages=4, max_len=64, scale=0.1, ws=FAKE, ws_bytes=None):
+        max_pages=4, max_len=64, scale=0.1, ws=FAKE, ws_bytes=None, sinks=None):
     if ws_bytes is None:
         ws_bytes = xa.attn_paged_decode_workspace_size(S, Hq, d, max_len)
     return _lib.lib().attn_paged_decode(q, kp, vp, bt, sl, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
-                                        scale, ws, ws_bytes, None)
+                                        scale, sinks, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(page=32), 2), (dict(d=96), 2), (dict(Hq=6, Hkv=4), 1), (dict(max_pages=3), 1),
     (dict(S=-1), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(sl=None), 1), (dict(bt=None), 1),
-    (dict(kp=FAKE + 2), 1), (dict(ws_bytes=16), 3), (dict(ws=None), 3),
+    (dict(kp=FAKE + 2), 1), (dict(ws_bytes=16), 3), (dict(ws=None), 3), (dict(sinks=FAKE + 1), 1),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
@@ -94,8 +96,8 @@ def test_workspace_size():
 
 
 def chunked(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qo=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128,
-            page=16, max_pages=4, max_len=64, max_q=32, scale=0.1, kind=1, window=0):
-    m = _lib.AttnMask(kind, window, None, 0)
+            page=16, max_pages=4, max_len=64, max_q=32, scale=0.1, kind=1, window=0, sink_tokens=0, sinks=None):
+    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks)
     return _lib.lib().attn_paged_prefill(q, kp, vp, bt, sl, qo, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
                                          max_q, scale, m, None)
 
@@ -106,6 +108,7 @@ def chunked(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qo=FAKE, o=FAKE, lse=FAK
     (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(q=None), 1), (dict(qo=None), 1),
     (dict(sl=None), 1), (dict(bt=None), 1), (dict(kp=FAKE + 2), 1), (dict(o=FAKE + 8), 1),
     (dict(max_len=1 << 29, max_pages=1 << 25), 2),
+    (dict(kind=1, sink_tokens=2), 1), (dict(sinks=FAKE + 2), 1),
 ])
 def test_paged_prefill_rejects_bad_arguments(kw, status):
     assert chunked(**kw) == status
