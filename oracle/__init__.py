@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     gather_sequence,
     paged_decode,
     paged_prefill,
+    attention_backward,
     to_f64,
     visibility,
 )

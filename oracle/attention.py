@@ -255,3 +255,57 @@ def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block
     if not outs_o:
         return np.zeros((0, Hq, d)), np.zeros((0, Hq))
     return np.concatenate(outs_o, axis=0), np.concatenate(outs_l, axis=0)
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                       mask: str = "none", window: int = 0, doc_offsets=None, sink_tokens: int = 0,
+                       sink_logits=None):
+    """Gradients of attention, in float64: (dq, dk, dv, dsink).
+
+    The backward pass the "Attention Is the Bottleneck" page describes for
+    FlashAttention-2: the forward keeps only O and the per-row log-sum-exp,
+    and the backward recomputes the probabilities from them.  Written here
+    from the chain rule of the plain definition, with full score rows:
+      P  = exp(S - LSE)                    (S = scale Q Kᵀ + mask; the sink,
+                                            if any, is inside LSE)
+      dV = Pᵀ dO,   dP = dO Vᵀ,   D = rowsum(dO ∘ O) = rowsum(P ∘ dP)
+      dS = P ∘ (dP - D),   dQ = scale dS K,   dK = scale dSᵀ Q
+      dsink[h] = -Σ_i P_sink,i D_i         (the sink's value is zero)
+    q, do [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d].  dk and dv sum over the query
+    heads of each KV head's group.  dsink is None without sink logits.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    sinks = None if sink_logits is None else np.asarray(sink_logits, dtype=np.float64).reshape(Hq)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsink = None if sinks is None else np.zeros(Hq)
+    vis = visibility(Nq, Nk, mask, window, doc_offsets, sink_tokens=sink_tokens)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            s = np.where(vis, scale * (q[b, h] @ k[b, hk].T), -np.inf)
+            cols = [s] if sinks is None else [s, np.full((Nq, 1), sinks[h])]
+            full = np.concatenate(cols, axis=1)
+            m = np.max(full, axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.exp(full - m)
+            l = e.sum(axis=1, keepdims=True)
+            p_all = e / np.where(l > 0, l, 1.0)
+            p = p_all[:, :Nk]
+            o = p @ v[b, hk]
+            dP = do[b, h] @ v[b, hk].T
+            D = np.sum(do[b, h] * o, axis=1, keepdims=True)
+            dS = p * (dP - D)
+            dq[b, h] = scale * (dS @ k[b, hk])
+            dk[b, hk] += scale * (dS.T @ q[b, h])
+            dv[b, hk] += p.T @ do[b, h]
+            if sinks is not None:
+                dsink[h] -= np.sum(p_all[:, Nk] * D[:, 0])
+    return dq, dk, dv, dsink

@@ -553,3 +553,100 @@ def test_paged_paths_carry_the_sink():
                                   np.arange(4), c["scale"], "causal", dtype="bf16", sink_logits=sinks)
     np.testing.assert_array_equal(op, o)
     np.testing.assert_array_equal(lp, lse)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, do, scale, mask, window, offsets, sink_tokens, sinks):
+    o, _ = oracle.attention(q, k, v, scale, mask, window, offsets, sink_tokens=sink_tokens, sink_logits=sinks)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("mask,window,offsets,Nq,Nk,sink_tokens,with_sinks", [
+    ("none", 0, None, 5, 6, 0, False), ("causal", 0, None, 6, 6, 0, False), ("causal", 0, None, 7, 5, 0, True),
+    ("window", 2, None, 6, 6, 1, True), ("document", 0, [0, 2, 5, 6], 6, 6, 0, False),
+])
+def test_backward_matches_central_differences(mask, window, offsets, Nq, Nk, sink_tokens, with_sinks):
+    B, Hq, Hkv, d = 1, 4, 2, 3
+    q, k, v = rnd(101, B, Hq, Nq, d), rnd(102, B, Hkv, Nk, d), rnd(103, B, Hkv, Nk, d)
+    do = rnd(104, B, Hq, Nq, d)
+    sinks = np.array([0.4, -0.8, 1.1, 0.0]) if with_sinks else None
+    scale = 0.7
+    dq, dk, dv, ds = oracle.attention_backward(q, k, v, do, scale, mask, window, offsets, sink_tokens, sinks)
+    h = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _loss(q, k, v, do, scale, mask, window, offsets, sink_tokens, sinks)
+            arr[idx] = old - h
+            lm = _loss(q, k, v, do, scale, mask, window, offsets, sink_tokens, sinks)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=1e-7, err_msg=name)
+    if with_sinks:
+        for hh in range(Hq):
+            sp, sm = sinks.copy(), sinks.copy()
+            sp[hh] += h
+            sm[hh] -= h
+            num = (_loss(q, k, v, do, scale, mask, window, offsets, sink_tokens, sp)
+                   - _loss(q, k, v, do, scale, mask, window, offsets, sink_tokens, sm)) / (2 * h)
+            assert abs(ds[hh] - num) < 1e-7
+    else:
+        assert ds is None
+
+
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("window", 9), ("none", 0)])
+def test_backward_matches_torch_autograd(mask, window):
+    # an independent forward written in torch (explicit masked softmax),
+    # differentiated by autograd in float64
+    import torch
+    B, Hq, Hkv, N, d = 2, 4, 2, 40, 16
+    q, k, v, do = rnd(111, B, Hq, N, d), rnd(112, B, Hkv, N, d), rnd(113, B, Hkv, N, d), rnd(114, B, Hq, N, d)
+    sinks = np.array([0.2, 1.5, -0.7, 3.0])
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ts = torch.tensor(sinks, requires_grad=True)
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    allowed = torch.ones(N, N, dtype=torch.bool) if mask == "none" else (j <= i)
+    if mask == "window":
+        allowed = allowed & (i - j < window)
+    kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+    s = 0.3 * tq @ kk.transpose(-1, -2)
+    s = s.masked_fill(~allowed, float("-inf"))
+    s = torch.cat([s, ts[None, :, None, None].expand(B, Hq, N, 1)], dim=-1)
+    p = torch.softmax(s, dim=-1)[..., :N]
+    (p @ vv * torch.tensor(do)).sum().backward()
+    dq, dk, dv, ds = oracle.attention_backward(q, k, v, do, 0.3, mask, window, sink_logits=sinks)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad), (ds, ts.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_key_shift_invariance_and_sink_sum():
+    # adding one vector to every visible key of a row shifts all its scores
+    # equally, which softmax ignores: without a sink the key gradients sum to
+    # zero; with a sink that sum is scale · Σ_i (Σ_j dS_ij) q_i, and
+    # Σ_ij dS_ij = -dsink (per head, no GQA here)
+    q, k, v, do = rnd(121, 1, 2, 12, 5), rnd(122, 1, 2, 12, 5), rnd(123, 1, 2, 12, 5), rnd(124, 1, 2, 12, 5)
+    _, dk, _, _ = oracle.attention_backward(q, k, v, do, 0.5, "causal")
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    sinks = np.array([0.5, -1.0])
+    _, dk_s, _, ds = oracle.attention_backward(q, k, v, do, 0.5, "none", sink_logits=sinks)
+    # with a sink, row i's key scores sum their gradient to Σ_j dS_ij =
+    # Σ_j P_ij dP_ij - D_i (1 - P_sink,i) = P_sink,i D_i, so
+    # Σ_j dK_j = scale Σ_i P_sink,i D_i q_i, while dsink = -Σ_i P_sink,i D_i
+    o, lse = oracle.attention(q, k, v, 0.5, "none", sink_logits=sinks)
+    D = np.sum(do * o, axis=-1)                                  # [1, H, N]
+    psink = np.exp(sinks[None, :, None] - lse)                   # [1, H, N]
+    want = 0.5 * np.einsum("bhn,bhnd->bhd", psink * D, q)
+    np.testing.assert_allclose(dk_s.sum(axis=2), want, atol=1e-12)
+    np.testing.assert_allclose(ds, -np.sum(psink * D, axis=(0, 2)), atol=1e-12)
+
+
+def test_backward_rows_that_see_nothing():
+    q, k, v, do = rnd(131, 1, 2, 8, 4), rnd(132, 1, 2, 5, 4), rnd(133, 1, 2, 5, 4), rnd(134, 1, 2, 8, 4)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.6, "causal")   # rows 0..2 see no key
+    assert np.all(dq[:, :, :3] == 0.0)
+    assert np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
