@@ -188,6 +188,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for counter collection: a few steps plus one known-size copy")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -242,6 +243,8 @@ def main() -> int:
         torch.cuda.synchronize()
         if not args.no_chunked:
             time_chunked(3, 0)
+        if not args.no_backward:
+            time_backward(pc, q, k, v, o, lse, doc, 3, 0)
         log("pmc pass done")
         return 0
 
@@ -318,11 +321,47 @@ def main() -> int:
     }
     if not args.no_chunked:
         result["chunked_prefill"] = time_chunked(K, W)
+    if not args.no_backward:
+        result["backward"] = time_backward(pc, q, k, v, o, lse, doc, K, W)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(pc, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def backward_flops(c: dict) -> int:
+    """The backward's five products per visible pair (recomputed scores, dP,
+    dV, dK, dQ), 2 d flops each."""
+    return 10 * c["d"] * c["B"] * c["Hq"] * visible_pairs(c["Nq"], c["Nk"], c["mask"], c["window"], c["doc_offsets"])
+
+
+def time_backward(pc: dict, q, k, v, o, lse, doc, K: int, W: int) -> dict:
+    """Backward of the headline prefill from its own o and lse (timed alone,
+    after the step loop): algorithmic TFLOP/s against the bf16 MFMA peak."""
+    import torch
+    from exact_io_aware_fwd_amd import attn_bwd, attn_bwd_workspace_size
+
+    do = to_dev(workloads.gen._draw(0, 5, (pc["B"], pc["Hq"], pc["Nq"], pc["d"]), "bf16"))
+    ws = torch.empty(attn_bwd_workspace_size(pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.uint8, device="cuda")
+    kw = dict(scale=pc["scale"], mask=pc["mask"], window=pc["window"], doc_offsets=doc, workspace=ws)
+
+    for _ in range(W):
+        attn_bwd(q, k, v, o, do, lse, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        attn_bwd(q, k, v, o, do, lse, **kw)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    flops = backward_flops(pc)
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"backward: {us:.1f} us, {tf:.1f} TFLOP/s")
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "us": round(us, 2), "flop_per_call": flops, "workload": f"backward of {PREFILL_CONFIG}",
+            "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel (one call)"}
 
 
 def time_chunked(K: int, W: int) -> dict:

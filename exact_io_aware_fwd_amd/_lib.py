@@ -48,6 +48,10 @@ def lib() -> ctypes.CDLL:
     L.attn_paged_decode.restype = i
     L.attn_paged_prefill.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, AttnMask, p]
     L.attn_paged_prefill.restype = i
+    L.attn_bwd_workspace_size.argtypes = [i, i, i]
+    L.attn_bwd_workspace_size.restype = sz
+    L.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, AttnMask, i, p, sz, p]
+    L.attn_bwd.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L

@@ -156,3 +156,36 @@ def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
                                        int(max_q_len), float(scale), m, _stream(stream))
     _lib.check(st)
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
+    return int(_lib.lib().attn_bwd_workspace_size(B, Hq, Nq))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+             lse: torch.Tensor, *, scale: float | None = None, mask: str = "none", window: int = 0,
+             doc_offsets: torch.Tensor | None = None, sink_tokens: int = 0,
+             sink_logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Attention backward from the forward's o and lse: -> (dq, dk, dv, dsink); dsink is None
+    without sink_logits.  bf16, d = 128; dk/dv sum over each KV head's query heads."""
+    _need(all(t.dim() == 4 for t in (q, k, v, o, do)), "q, k, v, o, do must be 4-d")
+    _need(all(t.dtype == torch.bfloat16 for t in (q, k, v, o, do)), "the backward is bf16")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v, o, do, lse)), "inputs must be contiguous device tensors")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(o.shape == q.shape and do.shape == q.shape and lse.shape == (B, Hq, Nq) and v.shape == k.shape, "shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = None if sink_logits is None else torch.empty(Hq, dtype=torch.float32, device=q.device)
+    need = attn_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq)
+    st = _lib.lib().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o), ctypes_ptr(do),
+                             ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk), ctypes_ptr(dv),
+                             None if dsink is None else ctypes_ptr(dsink), B, Hq, Hkv, Nq, Nk, d, float(scale), m,
+                             _lib.ATTN_DTYPE_BF16, ctypes_ptr(workspace), workspace.numel(), _stream(stream))
+    _lib.check(st)
+    return dq, dk, dv, dsink

@@ -13,6 +13,7 @@ int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t st
 }  // namespace xattn
 
 #include "decode_params.hpp"
+#include "backward_params.hpp"
 
 namespace {
 
@@ -178,5 +179,63 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
     p.sink_logits = mask.sink_logits;
     xattn::launch_paged_prefill_bf16(p, d, stream);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" size_t attn_bwd_workspace_size(int B, int Hq, int Nq) {
+    if (B < 0 || Hq < 0 || Nq < 0) return 0;
+    return xattn::backward_workspace_bytes(B, Hq, Nq);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, float* dsink,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, attn_mask mask, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind < ATTN_MASK_NONE || mask.kind > ATTN_MASK_DOCUMENT) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.kind == ATTN_MASK_DOCUMENT && (mask.num_docs < 1 || mask.doc_offsets == nullptr))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
+    if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (dtype != ATTN_DTYPE_BF16 || d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * Hkv * Nk == 0 && (long long)B * Hq * Nq == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr) {
+        if ((long long)B * Hq * Nq > 0) return ATTN_ERR_INVALID_ARGUMENT;
+    }
+    if ((long long)B * Hkv * Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+        return ATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)dsink & 3u) != 0)
+        return ATTN_ERR_INVALID_ARGUMENT;
+    const size_t need = xattn::backward_workspace_bytes(B, Hq, Nq);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
+    const long long q_tiles = (Nq + 127) / 128, k_tiles = (Nk + 127) / 128;
+    if ((long long)B * Hq * q_tiles > kMaxGrid || (long long)B * Hkv * k_tiles > kMaxGrid ||
+        (long long)B * Hq * Nq / 16 > kMaxGrid)
+        return ATTN_ERR_UNSUPPORTED;
+
+    xattn::BackwardParams p;
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o; p.dO = (const uint16_t*)dout; p.lse = lse;
+    p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv;
+    p.dsink = mask.sink_logits != nullptr ? dsink : nullptr;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.group = Hq / Hkv;
+    p.scale = scale;
+    p.scale_log2 = scale * xattn::kLog2e;
+    p.mask_kind = mask.kind;
+    p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? (mask.window < Nk ? mask.window : (Nk > 0 ? Nk : 1)) : 0;
+    p.doc_offsets = mask.kind == ATTN_MASK_DOCUMENT ? mask.doc_offsets : nullptr;
+    p.num_docs = mask.kind == ATTN_MASK_DOCUMENT ? mask.num_docs : 0;
+    p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
+    p.sink_logits = mask.sink_logits;
+    p.num_q_tiles = (int)q_tiles;
+    p.num_k_tiles = (int)k_tiles;
+    // with no query rows the dK/dV pass still runs and writes zeros
+    xattn::launch_backward(p, workspace, stream);
     return hip_status(hipGetLastError());
 }

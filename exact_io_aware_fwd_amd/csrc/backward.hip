@@ -1,0 +1,461 @@
+// Attention backward (bf16, head dim 128) by recomputation from the saved
+// log-sum-exp, the FlashAttention-2 backward ("Attention Is the Bottleneck",
+// FlashAttention-2 section: the forward keeps only O and the per-row
+// statistic; the backward recomputes the probabilities tile by tile).
+//
+//   P = exp(S - LSE),  D = rowsum(dO o O),  dS = P o (dO V^T - D)
+//   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q
+//
+// Three passes, no atomics on the gradients:
+//   prep   per query row: -LSE log2(e), D, the row's visible key interval,
+//          and the learned sink's gradient -sum_i P_sink,i D_i;
+//   dQ     one workgroup per (batch, query head, 128-row query tile), each
+//          wave owning 32 rows as in the forward; per 64-key tile it
+//          recomputes S^T = K Q^T and dP^T = V dO^T and accumulates
+//          dQ^T += K^T dS^T (the forward's O^T += V^T P^T with K and dS);
+//   dK/dV  one workgroup per (batch, KV head, 128-key tile), each wave owning
+//          32 keys in registers; it streams 64-row query tiles of every query
+//          head of the group, recomputes S = Q K^T and dP = dO V^T with the
+//          keys as the accumulator columns, and accumulates dV^T += dO^T P
+//          and dK^T += Q^T dS.
+// Tiles that one product reads by rows and another transposed are copied to
+// LDS twice, once in each padded layout, so every read is conflict-free.
+#include "backward_params.hpp"
+#include "prefill_tiles.hpp"
+
+namespace xattn {
+
+namespace {
+
+constexpr int kBD = 128;   // head dim of this build of the backward
+
+// A operand of a 32x32x16 MFMA read by rows from a row-padded tile: row
+// (lane & 31) + 32 jb, head-dim chunk 2 kk + (lane >> 5).  rl = this lane's
+// base, tile + (lane & 31) * KS * 16 + (lane >> 5) * 16.
+__device__ __forceinline__ bf16x8 row_operand(const uint8_t* rl, int jb, int kk) {
+    using C = PrefillBf16Cfg<kBD>;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(rl + jb * 32 * C::KS * 16 + kk * 32));
+}
+
+// A operand of a 32x32x16 MFMA read transposed from a transpose-padded tile
+// (two ds_read_b64_tr_b16): column cb*32 + (lane & 31) of tile rows
+// kb*16 + 8 (t / 4) + 4 (lane >> 5) + t % 4, t = 0..7, the row order of the
+// B operand built from a 32x32 accumulator (see pack_operands).  tl = this
+// lane's base, tile + vbase.
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tl, int kb, int cb) {
+    using C = PrefillBf16Cfg<kBD>;
+    const uint8_t* vp = tl + kb * 16 * C::VS * 16 + cb * 64;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+}
+
+// acc[jb] = sum_kk A(rows of the tile) x bf[kk]: a 64 x 32 product over the
+// head dim (16 MFMAs).
+__device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)[kBD / 16], f32x16 (&acc)[2]) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < kBD / 16; ++kk)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+            acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(rl, jb, kk), bf[kk], acc[jb], 0, 0, 0);
+}
+
+// acc[cb] += sum_kb A(transposed tile) x pf[kb]: a (d x 64) by (64 x 32)
+// product accumulated into a 128 x 32 accumulator (16 MFMAs).
+__device__ __forceinline__ void tr_times(const uint8_t* tl, const bf16x8 (&pf)[4], f32x16 (&acc)[kBD / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int cb = 0; cb < kBD / 32; ++cb)
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(tl, kb, cb), pf[kb], acc[cb], 0, 0, 0);
+}
+
+// A 64 x 32 accumulator pair as the bf16 B operand of the next product, one
+// per 16-row block (the register order of a 32x32 accumulator is the
+// permuted row order tr_operand reads).
+__device__ __forceinline__ void pack_operands(const f32x16 (&x)[2], bf16x8 (&pf)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int jb = kb >> 1, h = (kb & 1) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[jb][h + 2 * e], x[jb][h + 2 * e + 1]);
+        pf[kb] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// Store a d x 32 accumulator (column = this lane's row or key) as one bf16
+// row of d values, times `mul`.
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[kBD / 32], float mul, int lane) {
+#pragma unroll
+    for (int cb = 0; cb < kBD / 32; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[cb][4 * gq + 0] * mul, acc[cb][4 * gq + 1] * mul);
+            w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * mul, acc[cb][4 * gq + 3] * mul);
+            *(u32x2*)(dst + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
+        }
+}
+
+// The B operand fragment of a row held in registers (query row for dQ, key
+// for dK/dV): chunks (lane >> 5) * 8 .. + 8 of every 16-wide head-dim step.
+__device__ __forceinline__ void load_fragment(const uint16_t* rowp, bool ok, int lane, bf16x8 (&f)[kBD / 16]) {
+#pragma unroll
+    for (int kk = 0; kk < kBD / 16; ++kk) {
+        const u32x4 w = ok ? *(const u32x4*)(rowp + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+        f[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+__device__ __forceinline__ PrefillParams mask_params(const BackwardParams& p) {
+    PrefillParams m;
+    m.Nq = p.Nq;
+    m.Nk = p.Nk;
+    m.mask_kind = p.mask_kind;
+    m.window = p.window;
+    m.doc_offsets = p.doc_offsets;
+    m.num_docs = p.num_docs;
+    m.sink_end = p.sink_end;
+    return m;
+}
+
+}  // namespace
+
+__global__ void bwd_zero_kernel(float* x, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = 0.f;
+}
+
+// 16 threads per query row: D = dO . O over 128 columns, plus the row's
+// statistics for the two gradient passes.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) {
+    const int t = threadIdx.x;
+    const long long rows = (long long)p.B * p.Hq * p.Nq;
+    const long long rg = (long long)blockIdx.x * 16 + t / 16;
+    float acc = 0.f;
+    if (rg < rows) {
+        const u32x4 a = *(const u32x4*)(p.o + rg * kBD + (t % 16) * 8);
+        const u32x4 g = *(const u32x4*)(p.dO + rg * kBD + (t % 16) * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (rg < rows && t % 16 == 0) {
+        const int i = (int)(rg % p.Nq);
+        const int h = (int)((rg / p.Nq) % p.Hq);
+        const float L = p.lse[rg];
+        p.ws_d[rg] = acc;
+        p.ws_nl[rg] = L > -__builtin_inff() ? -L * kLog2e : 0.f;
+        const PrefillParams m = mask_params(p);
+        int lo, hi;
+        row_interval(m, i, lo, hi);
+        p.ws_lo[rg] = lo;
+        p.ws_hi[rg] = hi;
+        if (p.dsink != nullptr && p.sink_logits != nullptr && L > -__builtin_inff())
+            atomicAdd(p.dsink + h, -__builtin_amdgcn_exp2f((p.sink_logits[h] - L) * kLog2e) * acc);
+    }
+}
+
+// dQ: per 64-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
+// dQ^T += K^T dS^T.  K is copied twice (row and transposed layouts), V once.
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardParams p) {
+    using C = PrefillBf16Cfg<kBD>;
+    __shared__ __attribute__((aligned(1024))) uint8_t kr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t kr1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vr1[C::KTILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bk, qt, g;
+    decode_work(blockIdx.x, p.B * p.Hkv, p.num_q_tiles, p.group, bk, qt, g);
+    const int b = bk / p.Hkv, hkv = bk % p.Hkv, hq = hkv * p.group + g;
+    const PrefillParams m = mask_params(p);
+
+    const int r0 = qt * C::BM;
+    const int r_last = min(r0 + C::BM, p.Nq) - 1;
+    const int w0 = r0 + wave * 32;
+    const int w_last = min(w0 + 31, p.Nq - 1);
+    const int row = w0 + (lane & 31);
+    const bool row_ok = row < p.Nq;
+    int lo_i, hi_i, lo_wg, hi_wg, tmp, lo_w_first, hi_w_first, lo_w_last, hi_w_last;
+    row_interval(m, row, lo_i, hi_i);
+    row_interval(m, r0, lo_wg, tmp);
+    row_interval(m, r_last, tmp, hi_wg);
+    row_interval(m, w0, lo_w_first, hi_w_first);
+    row_interval(m, w_last, lo_w_last, hi_w_last);
+    const bool wave_has_rows = w0 < p.Nq;
+
+    const size_t head_row = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    bf16x8 qf[kBD / 16], df[kBD / 16];
+    load_fragment(p.q + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, qf);
+    load_fragment(p.dO + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, df);
+    // rows past Nq get weight 0 (their -LSE is -inf) and D = 0
+    const float nl = row_ok ? p.ws_nl[head_row + row] : -__builtin_inff();
+    const float Drow = row_ok ? p.ws_d[head_row + row] : 0.f;
+
+    f32x16 acc[kBD / 32];
+#pragma unroll
+    for (int cb = 0; cb < kBD / 32; ++cb) acc[cb] = f32x16{};
+
+    const uint16_t* kg_ = p.k + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * kBD;
+    const uint16_t* vg_ = p.v + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * kBD;
+    const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, C::BN);
+    uint32_t koff[C::KLW], voff[C::VLW];
+    tile_src_offsets<kBD, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<kBD, C::VS, C::VLOADS>(voff, wave, lane);
+    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+
+    auto copy = [&](int t, uint8_t* kr, uint8_t* kt, uint8_t* vr) __attribute__((always_inline)) {
+        load_tile_async<kBD, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kr, koff, wave);
+        load_tile_async<kBD, C::VS, C::VLOADS>(kg_, t * C::BN, p.Nk, kt, voff, wave);
+        load_tile_async<kBD, C::KS, C::KLOADS>(vg_, t * C::BN, p.Nk, vr, koff, wave);
+    };
+    auto stage = [&](int it, const uint8_t* kr, const uint8_t* kt, const uint8_t* vr, uint8_t* krn, uint8_t* ktn,
+                     uint8_t* vrn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of this tile landed
+        __syncthreads();
+        if (it + 1 < tr.n) copy(tile_of(tr, it + 1), krn, ktn, vrn);
+        const int n0 = tile_of(tr, it) * C::BN;
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < p.sink_end);
+        if (!active) return;
+        const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < p.sink_end);
+        f32x16 s[2], dp[2];
+        rows_times(kr + kbase, qf, s);    // S^T = K Q^T
+        rows_times(vr + kbase, df, dp);   // dP^T = V dO^T
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl));
+                if (!full && (key > hi_i || (key < lo_i && key >= p.sink_end))) pr = 0.f;
+                s[jb][r] = pr * (dp[jb][r] - Drow);   // dS^T
+            }
+        bf16x8 dsf[4];
+        pack_operands(s, dsf);
+        tr_times(kt + vbase, dsf, acc);   // dQ^T += K^T dS^T
+    };
+
+    if (tr.n > 0) {
+        copy(tile_of(tr, 0), kr0, kt0, vr0);
+        for (int it = 0; it < tr.n; it += 2) {
+            stage(it, kr0, kt0, vr0, kr1, kt1, vr1);
+            if (it + 1 < tr.n) stage(it + 1, kr1, kt1, vr1, kr0, kt0, vr0);
+        }
+    }
+    if (row_ok) store_row(p.dq + (head_row + row) * kBD, acc, p.scale, lane);
+}
+
+// dK and dV: each wave owns 32 keys (K and V fragments in registers) and
+// streams 64-row query tiles of every query head of its group.
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
+    using C = PrefillBf16Cfg<kBD>;
+    constexpr int BQ = 64;    // query rows per streamed tile
+    constexpr int BK = 128;   // keys per workgroup
+    __shared__ __attribute__((aligned(1024))) uint8_t qr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qt0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dt0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qr1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qt1[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dt1[C::VTILE];
+    // per tile row: -LSE log2 e, D, lo, hi (256 bytes each)
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[4 * BQ * 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[4 * BQ * 4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nbk = p.B * p.Hkv;
+    const int kt_idx = blockIdx.x / nbk;     // key tiles in order: under causal masks the first are the heaviest
+    const int bk = blockIdx.x % nbk;
+    const int b = bk / p.Hkv, hkv = bk % p.Hkv;
+    const PrefillParams m = mask_params(p);
+
+    const int k0 = kt_idx * BK;
+    const int k0w = k0 + wave * 32;
+    const int key = k0w + (lane & 31);
+    const bool key_ok = key < p.Nk;
+    const int k_last = min(k0 + BK, p.Nk) - 1;
+
+    const size_t kv_head = ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk;
+    bf16x8 kf[kBD / 16], vf[kBD / 16];
+    load_fragment(p.k + (kv_head + (key_ok ? key : 0)) * kBD, key_ok, lane, kf);
+    load_fragment(p.v + (kv_head + (key_ok ? key : 0)) * kBD, key_ok, lane, vf);
+    f32x16 dk[kBD / 32], dv[kBD / 32];
+#pragma unroll
+    for (int cb = 0; cb < kBD / 32; ++cb) {
+        dk[cb] = f32x16{};
+        dv[cb] = f32x16{};
+    }
+
+    // Query rows that see any key of [k0, k_last]: from the first row whose
+    // interval reaches k0 to the last whose interval starts at or before
+    // k_last (every later row, when sink keys are in the tile).  Both ends
+    // are monotone in the row, so two binary searches find them.
+    int first = p.Nq, last = -1;
+    {
+        int a = 0, z = p.Nq;
+        while (a < z) {
+            const int mid = (a + z) >> 1;
+            int l, h;
+            row_interval(m, mid, l, h);
+            if (h >= k0) z = mid; else a = mid + 1;
+        }
+        first = a;
+        if (k0 < p.sink_end) {
+            last = p.Nq - 1;
+        } else {
+            a = -1;
+            z = p.Nq - 1;
+            while (a < z) {
+                const int mid = (a + z + 1) >> 1;
+                int l, h;
+                row_interval(m, mid, l, h);
+                if (l <= k_last) a = mid; else z = mid - 1;
+            }
+            last = a;
+        }
+    }
+    const int qt_first = first / BQ;
+    const int ntq = (first <= last && k0 < p.Nk) ? last / BQ - qt_first + 1 : 0;
+    const int n_iter = ntq * p.group;
+
+    uint32_t koff[C::KLW], voff[C::VLW];
+    tile_src_offsets<kBD, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<kBD, C::VS, C::VLOADS>(voff, wave, lane);
+    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+
+    auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * p.group + it / ntq; };
+    auto q0_of = [&](int it) __attribute__((always_inline)) { return (qt_first + it % ntq) * BQ; };
+    // copies of iteration it: Q and dO rows in both layouts, and the rows' statistics
+    auto copy = [&](int it, uint8_t* qr, uint8_t* qt, uint8_t* dr, uint8_t* dt, uint8_t* st)
+        __attribute__((always_inline)) {
+        const size_t head_row = ((size_t)b * p.Hq + head_of(it)) * (size_t)p.Nq;
+        const int q0 = q0_of(it);
+        const uint16_t* qg = p.q + head_row * kBD;
+        const uint16_t* dg = p.dO + head_row * kBD;
+        load_tile_async<kBD, C::KS, C::KLOADS>(qg, q0, p.Nq, qr, koff, wave);
+        load_tile_async<kBD, C::VS, C::VLOADS>(qg, q0, p.Nq, qt, voff, wave);
+        load_tile_async<kBD, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
+        load_tile_async<kBD, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
+        if (wave == 0) {
+            const int nrow = (p.Nq - q0) * 4;   // bytes of rows that exist; the rest read 0
+            const void* srcs[4] = {p.ws_nl + head_row + q0, p.ws_d + head_row + q0, p.ws_lo + head_row + q0,
+                                   p.ws_hi + head_row + q0};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srcs[a], (short)0, nrow, 0x00020000);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + a * BQ * 4), 4, lane * 4, 0, 0, 0);
+            }
+        }
+    };
+
+    auto stage = [&](int it, const uint8_t* qr, const uint8_t* qt, const uint8_t* dr, const uint8_t* dt,
+                     const uint8_t* st, uint8_t* qrn, uint8_t* qtn, uint8_t* drn, uint8_t* dtn, uint8_t* stn)
+        __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        if (it + 1 < n_iter) copy(it + 1, qrn, qtn, drn, dtn, stn);
+        const int q0 = q0_of(it);
+        const int q_end = min(q0 + BQ, p.Nq) - 1;
+        int lo_a, hi_a, lo_z, hi_z;
+        row_interval(m, q0, lo_a, hi_a);
+        row_interval(m, q_end, lo_z, hi_z);
+        // does some row of the tile see some key of this wave (its keys exist)?
+        if (!(k0w < p.Nk && hi_z >= k0w && (lo_a <= k0w + 31 || k0w < p.sink_end))) return;
+        const bool full = q0 + BQ - 1 < p.Nq && k0w + 31 < p.Nk && hi_a >= k0w + 31 &&
+                          (lo_z <= k0w || k0w + 31 < p.sink_end);
+        f32x16 s[2], dp[2];
+        rows_times(qr + kbase, kf, s);    // S = Q K^T   (columns: this lane's key)
+        rows_times(dr + kbase, vf, dp);   // dP = dO V^T
+        const float* nl = (const float*)st;
+        const float* dd = (const float*)(st + BQ * 4);
+        const int32_t* rlo = (const int32_t*)(st + 2 * BQ * 4);
+        const int32_t* rhi = (const int32_t*)(st + 3 * BQ * 4);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int rb = jb * 32 + 8 * g4 + 4 * (lane >> 5);   // first of this lane's 4 consecutive rows
+                const f32x4 nl4 = *(const f32x4*)(nl + rb);
+                const f32x4 dd4 = *(const f32x4*)(dd + rb);
+                int32_t lo4[4] = {0, 0, 0, 0}, hi4[4] = {0, 0, 0, 0};
+                if (!full) {
+                    const u32x4 a = *(const u32x4*)(rlo + rb);
+                    const u32x4 z = *(const u32x4*)(rhi + rb);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lo4[e] = (int32_t)a[e];
+                        hi4[e] = (int32_t)z[e];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[e]));
+                    if (!full) {
+                        const bool vis = q0 + rb + e < p.Nq && key <= hi4[e] && (key >= lo4[e] || key < p.sink_end);
+                        if (!vis) pr = 0.f;
+                    }
+                    dp[jb][r] = pr * (dp[jb][r] - dd4[e]);   // dS
+                    s[jb][r] = pr;                            // P
+                }
+            }
+        bf16x8 pf[4], dsf[4];
+        pack_operands(s, pf);
+        pack_operands(dp, dsf);
+        tr_times(dt + vbase, pf, dv);    // dV^T += dO^T P
+        tr_times(qt + vbase, dsf, dk);   // dK^T += Q^T dS
+    };
+
+    if (n_iter > 0) {
+        copy(0, qr0, qt0, dr0, dt0, st0);
+        for (int it = 0; it < n_iter; it += 2) {
+            stage(it, qr0, qt0, dr0, dt0, st0, qr1, qt1, dr1, dt1, st1);
+            if (it + 1 < n_iter) stage(it + 1, qr1, qt1, dr1, dt1, st1, qr0, qt0, dr0, dt0, st0);
+        }
+    }
+    if (key_ok) {
+        store_row(p.dk + (kv_head + key) * kBD, dk, p.scale, lane);
+        store_row(p.dv + (kv_head + key) * kBD, dv, 1.f, lane);
+    }
+}
+
+size_t backward_workspace_bytes(int B, int Hq, int Nq) {
+    const size_t rows = (size_t)B * Hq * Nq;
+    return 4 * ((rows * 4 + 255) / 256) * 256;
+}
+
+int launch_backward(BackwardParams p, void* ws, hipStream_t stream) {
+    const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+    const size_t stride = ((rows * 4 + 255) / 256) * 256;
+    p.ws_nl = (float*)ws;
+    p.ws_d = (float*)((char*)ws + stride);
+    p.ws_lo = (int32_t*)((char*)ws + 2 * stride);
+    p.ws_hi = (int32_t*)((char*)ws + 3 * stride);
+    // the sink gradient accumulates across rows: clear it with a kernel (not a
+    // memset, so the sequence can be captured into a graph)
+    if (p.dsink != nullptr && p.Hq > 0)
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((p.Hq + 255) / 256), dim3(256), 0, stream, p.dsink, p.Hq);
+    if (rows > 0) {
+        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
+    }
+    if ((long long)p.B * p.Hkv * p.num_k_tiles > 0)
+        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
+    return 0;
+}
+
+}  // namespace xattn

@@ -20,33 +20,9 @@
 // Softmax runs in base 2: scores are scaled by scale*log2(e) with one FMA that
 // also subtracts the running max, then v_exp_f32.  The division by the row sum
 // happens once at the end (delayed normalisation, FlashAttention-2 section).
-#include "common.hpp"
+#include "prefill_tiles.hpp"
 
 namespace xattn {
-
-template <int D>
-struct PrefillBf16Cfg {
-    static constexpr int BM = 128;               // query rows per workgroup (4 waves x 32)
-    static constexpr int BN = 64;                // keys per K/V tile
-    static constexpr int CHUNKS = D / 8;         // 16-byte chunks per K/V row
-    // Row strides in LDS, in 16-byte slots (LDS serves 256 bytes per cycle).
-    // One slot of padding per K row puts 16 consecutive rows on 16 different
-    // 16-byte bank groups (the K operand reads one chunk of 16 consecutive
-    // rows).  Four slots per V row put 4 consecutive rows x 64 bytes on
-    // distinct banks (the transposed V reads of 32 lanes: 4 key rows x 32
-    // columns).
-    static constexpr int KS = CHUNKS + 1;
-    static constexpr int VS = CHUNKS + 4;
-    static constexpr int KTILE = BN * KS * 16;   // bytes per K tile in LDS
-    static constexpr int VTILE = BN * VS * 16;
-    static constexpr int KLOADS = KTILE / 1024;  // 1 KiB direct loads per K tile
-    static constexpr int VLOADS = VTILE / 1024;
-    static constexpr int KLW = (KLOADS + 3) / 4; // per wave (rounded up)
-    static constexpr int VLW = (VLOADS + 3) / 4;
-    static constexpr int DK = D / 16;            // MFMA steps over the head dim for S
-    static constexpr int CB = D / 32;            // 32-wide blocks of the head dim for O
-    static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "tiles must be whole 1 KiB blocks");
-};
 
 // Softmax weights are kept relative to a stale row max until a tile's max
 // exceeds it by more than 2^8; only then is the accumulator rescaled (the
@@ -54,44 +30,6 @@ struct PrefillBf16Cfg {
 // Weights stay below 256, well inside fp32 and bf16 range, and the result is
 // unchanged because O and the row sums share the same reference.
 constexpr float kRescaleThreshold = 8.f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Per-lane byte offsets into one K or V tile in global memory for this wave's
-// direct loads.  Load i of the tile fills LDS bytes [1024 i, 1024 i + 1024):
-// lane l lands on 16-byte slot 64 i + l, i.e. row (64 i + l) / S, chunk
-// (64 i + l) % S of the padded layout.  Padding slots fetch the row's last
-// chunk again (never read back).
-template <int D, int S, int NL>
-__device__ __forceinline__ void tile_src_offsets(uint32_t (&off)[(NL + 3) / 4], int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < (NL + 3) / 4; ++j) {
-        const int slot = (wave + 4 * j) * 64 + lane;
-        const int r = slot / S;
-        int c = slot % S;
-        c = c < D / 8 ? c : D / 8 - 1;
-        off[j] = (uint32_t)((r * D + c * 8) * 2);
-    }
-}
-
-// Issue this wave's share of the direct HBM -> LDS copies of one tile
-// (buffer_load_dwordx4 ... lds).  The buffer resource starts at key n0 and
-// covers only the keys that exist, so rows past Nk read as zeros.
-template <int D, int S, int NL>
-__device__ __forceinline__ void load_tile_async(const uint16_t* __restrict__ base, int n0, int Nk, uint8_t* lds,
-                                                const uint32_t (&off)[(NL + 3) / 4], int wave) {
-    const int rows = Nk - n0;
-    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (size_t)n0 * D), (short)0, rows * D * 2, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < (NL + 3) / 4; ++j) {
-        const int blk = wave + 4 * j;
-        if (NL % 4 == 0 || blk < NL)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 1024), 16, off[j], 0, 0, 0);
-    }
-}
 
 template <int D>
 struct PrefillBf16State {
@@ -203,9 +141,12 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
         }
 }
 
-template <int D>
+// SINKS: the window mask keeps sink tokens visible (the second key interval);
+// without it the tile loop and the mask compile to the one-interval form.
+template <int D, bool SINKS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     using C = PrefillBf16Cfg<D>;
+    const int sink_end = SINKS ? p.sink_end : 0;
     // two stages of the K/V ring, as separate arrays so each access names its buffer
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::VTILE];
@@ -257,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     st.l_run = 0.f;
     st.l_f32 = 0.f;
 
-    const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, C::BN);
+    const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
     uint32_t koff[C::KLW], voff[C::VLW];
     tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
@@ -279,10 +220,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
             load_tile_async<D, C::VS, C::VLOADS>(vg_, tn * C::BN, p.Nk, vn, voff, wave);
         }
         const int n0 = tile_of(tr, it) * C::BN;
-        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < p.sink_end);
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
         if (active) {
-            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < p.sink_end);
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, p.sink_end, p.scale_log2, lane);
+            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
         }
     };
 
@@ -362,9 +303,10 @@ __device__ __forceinline__ void load_paged_tile_async(const uint16_t* __restrict
     }
 }
 
-template <int D>
+template <int D, bool SINKS>
 __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefillParams pp) {
     using C = PrefillBf16Cfg<D>;
+    const int sink_end = SINKS ? pp.sink_end : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::VTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::KTILE];
@@ -390,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     p.window = pp.window;
     p.doc_offsets = nullptr;
     p.num_docs = 0;
-    p.sink_end = pp.sink_end;
+    p.sink_end = sink_end;
 
     const int r_last = min(r0 + C::BM, nq) - 1;
     const int w0 = r0 + wave * 32;
@@ -424,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     st.l_run = 0.f;
     st.l_f32 = 0.f;
 
-    const TileRange tr = tile_range(lo_wg, hi_wg, pp.sink_end, C::BN);
+    const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
     uint32_t krc[C::KLW], vrc[C::VLW];
     tile_rows_chunks<D, C::KS, C::KLOADS>(krc, wave, lane);
@@ -471,10 +413,10 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
             if (it + 2 < tr.n) next = entries(tile_of(tr, it + 2));
         }
         const int n0 = tile_of(tr, it) * C::BN;
-        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < pp.sink_end);
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
         if (active) {
-            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < pp.sink_end);
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, pp.sink_end, pp.scale_log2, lane);
+            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
+            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
         }
     };
 
@@ -510,10 +452,14 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
 
 int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t stream) {
     const int blocks = p.num_seqs * p.Hq * p.num_q_tiles;
-    if (d == 128)
-        hipLaunchKernelGGL(paged_prefill_bf16_kernel<128>, dim3(blocks), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(paged_prefill_bf16_kernel<64>, dim3(blocks), dim3(256), 0, stream, p);
+    const bool sinks = p.sink_end > 0;
+    if (d == 128) {
+        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, p);
+    } else {
+        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
+    }
     return 0;
 }
 
@@ -521,10 +467,14 @@ int prefill_bf16_rows_per_block() { return PrefillBf16Cfg<128>::BM; }
 
 int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
     const int blocks = p.B * p.Hq * p.num_q_tiles;
-    if (d == 128)
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(blocks), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(blocks), dim3(256), 0, stream, p);
+    const bool sinks = p.sink_end > 0;
+    if (d == 128) {
+        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, p);
+    } else {
+        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
+    }
     return 0;
 }
 

@@ -201,6 +201,40 @@ int attn_paged_prefill(const void* q, const void* k_pages, const void* v_pages,
                        int max_pages_per_seq, int max_seq_len, int max_q_len, float scale,
                        attn_mask mask, hipStream_t stream);
 
+/*
+ * attn_bwd_workspace_size — bytes of scratch device memory attn_bwd needs
+ * (four per-row statistics of 4 bytes).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
+
+/*
+ * attn_bwd — gradients of attn_fwd by recomputation from its saved
+ * statistic: the forward keeps only O and the per-row LSE, and the backward
+ * recomputes the probabilities tile by tile ("Attention Is the Bottleneck",
+ * FlashAttention-2 section).  With P = exp(scale Q K^T + mask - LSE),
+ * D = rowsum(dO o O) and dS = P o (dO V^T - D):
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dO,
+ * dk and dv summed over the query heads of each KV head's group, and, with
+ * learned sink logits, dsink[h] = -sum over rows of P_sink D.
+ *
+ *   q, o, dout   [B, Hq, Nq, d]   bf16, read only (o and lse from attn_fwd
+ *                                 with the same arguments)
+ *   k, v         [B, Hkv, Nk, d]  bf16, read only
+ *   lse          [B, Hq, Nq]      float32, read only
+ *   dq           [B, Hq, Nq, d]   bf16, written in full
+ *   dk, dv       [B, Hkv, Nk, d]  bf16, written in full (0 for keys no row sees)
+ *   dsink        NULL or [Hq] float32, written when mask.sink_logits is given
+ *   workspace    device scratch of at least attn_bwd_workspace_size(B, Hq, Nq)
+ *                bytes, 16-byte aligned; not to be shared by concurrent calls
+ *
+ * Every mask kind and both sink forms apply as in attn_fwd.  This build
+ * supports dtype BF16 with d = 128 (anything else: ATTN_ERR_UNSUPPORTED).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* dsink,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, attn_mask mask, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Text for a status code (static storage; for ATTN_ERR_HIP, thread-local). */
 const char* attn_status_string(int status);
 

@@ -19,9 +19,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_five_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_paged_decode", "attn_paged_decode_workspace_size",
-                                    "attn_paged_prefill", "attn_status_string"]
+def test_header_declares_the_seven_entry_points():
+    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_paged_decode",
+                                    "attn_paged_decode_workspace_size", "attn_paged_prefill", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -117,3 +117,28 @@ def test_paged_prefill_rejects_bad_arguments(kw, status):
 def test_paged_prefill_empty_problems_are_noops():
     assert chunked(q=None, kp=None, vp=None, bt=None, sl=None, qo=None, o=None, lse=None, S=0) == 0
     assert chunked(q=None, kp=None, vp=None, bt=None, sl=None, qo=None, o=None, lse=None, max_q=0) == 0
+
+
+def bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dsink=None, B=1, Hq=4, Hkv=2,
+        Nq=16, Nk=16, d=128, scale=0.1, kind=1, window=0, dtype=1, ws=FAKE, ws_bytes=None, sink_tokens=0, sinks=None):
+    if ws_bytes is None:
+        ws_bytes = xa.attn_bwd_workspace_size(B, Hq, Nq)
+    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks)
+    return _lib.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, dsink, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype,
+                               ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), 2), (dict(dtype=0), 2), (dict(dtype=5), 1), (dict(Hq=6, Hkv=4), 1), (dict(B=-1), 1),
+    (dict(scale=0.0), 1), (dict(kind=9), 1), (dict(kind=2, window=0), 1), (dict(kind=1, sink_tokens=3), 1),
+    (dict(q=None), 1), (dict(do=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(dq=FAKE + 8), 1),
+    (dict(lse=FAKE + 2), 1), (dict(ws_bytes=8), 3), (dict(ws=None), 3), (dict(Nk=1 << 29), 2),
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    assert xa.attn_bwd_workspace_size(2, 4, 100) == 4 * (((2 * 4 * 100 * 4) + 255) // 256) * 256
+    assert xa.attn_bwd_workspace_size(-1, 4, 100) == 0
+    assert bwd(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, B=0) == 0

@@ -1,0 +1,84 @@
+"""Backward pass on the GPU against the fp64 oracle's gradients: dq, dk, dv
+(and the learned sinks' gradient) after the GPU forward, over every mask kind,
+GQA, ragged sizes, rows that see nothing and both sink forms.
+
+Tolerance (no stated bound covers gradients; derived from the arithmetic):
+P and dS enter their products rounded to bf16 (relative 2^-9 each) and D
+uses the forward's bf16 output, so errors of a few tenths of a percent of the
+gradient's scale are expected; the bound is 2e-2 relative Frobenius error
+per tensor and 2e-2 x max|reference| on every element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from exact_io_aware_fwd_amd import attn_bwd, attn_fwd
+from _gpu_helpers import dev, doc_tensor, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 2e-2
+REL_MAX = 2e-2
+
+
+def check_grad(got, want, label):
+    err = np.abs(got - want)
+    scale = float(np.abs(want).max()) if want.size else 0.0
+    fro = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    say(f"[grad] {label}: rel-fro {fro:.3e} max-abs {float(err.max()) if err.size else 0.0:.3e} (scale {scale:.3e})")
+    assert np.all(np.isfinite(got)), f"{label}: non-finite gradient"
+    if scale == 0.0:
+        assert np.all(got == 0.0), f"{label}: gradient must be 0"
+        return
+    assert fro <= REL_FRO, f"{label}: relative Frobenius error {fro}"
+    assert float(err.max()) <= REL_MAX * scale, f"{label}: max-abs {float(err.max())} > {REL_MAX} x {scale}"
+
+
+def run_case(c, label, sink_tokens=0, sinks=None):
+    say(f"[case] {label} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} Nq={c['Nq']} Nk={c['Nk']} mask={c['mask']} "
+        f"window={c['window']} sink_tokens={sink_tokens} sinks={'yes' if sinks is not None else 'no'}")
+    q, k, v, do = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16"), dev(c["do"], "bf16")
+    sl = None if sinks is None else torch.from_numpy(sinks).cuda()
+    kw = dict(scale=c["scale"], mask=c["mask"], window=c["window"], doc_offsets=doc_tensor(c),
+              sink_tokens=sink_tokens, sink_logits=sl)
+    o, lse = attn_fwd(q, k, v, **kw)
+    dq, dk, dv, ds = attn_bwd(q, k, v, o, do, lse, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(oracle.to_f64(c["q"], "bf16"), oracle.to_f64(c["k"], "bf16"),
+                                    oracle.to_f64(c["v"], "bf16"), oracle.to_f64(c["do"], "bf16"), c["scale"],
+                                    c["mask"], c["window"], c["doc_offsets"], sink_tokens,
+                                    None if sinks is None else sinks.astype(np.float64))
+    for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        check_grad(host_f64(got), want, f"{label} {name}")
+    if sinks is not None:
+        check_grad(host_f64(ds), ref[3], f"{label} dsink")
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 100), ("document", 0)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)])
+def test_backward_masks(mask, window, Hq, Hkv):
+    c = workloads.make_backward(1, Hq, Hkv, 600, 600, 128, seed=71, mask=mask, window=window, doc_min=80,
+                                doc_max=300)
+    run_case(c, f"bwd {mask} Hq{Hq}Hkv{Hkv}")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(300, 200), (129, 500), (65, 65), (1, 130)])
+def test_backward_ragged_and_aligned(Nq, Nk):
+    # causal, bottom-right: Nq > Nk leaves the first rows with no key
+    c = workloads.make_backward(2, 4, 2, Nq, Nk, 128, seed=73, mask="causal")
+    run_case(c, f"bwd causal {Nq}x{Nk}")
+
+
+@pytest.mark.parametrize("sink_tokens,with_logits", [(4, True), (70, False), (0, True)])
+def test_backward_sinks(sink_tokens, with_logits):
+    c = workloads.make_backward(1, 8, 2, 500, 500, 128, seed=75, mask="window", window=96)
+    sinks = None
+    if with_logits:
+        sinks = np.random.default_rng(76).normal(0.0, 2.0, 8).astype(np.float32)
+    run_case(c, f"bwd window96 sinks{sink_tokens}", sink_tokens, sinks)
+
+
+def test_backward_larger_causal():
+    c = workloads.make_backward(1, 8, 2, 2048, 2048, 128, seed=77, mask="causal")
+    run_case(c, "bwd causal 2048 GQA")

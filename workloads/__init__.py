@@ -14,5 +14,6 @@ from .gen import (  # noqa: F401
     prefill_config,
     decode_config,
     make_chunked_prefill,
+    make_backward,
     chunked_config,
 )

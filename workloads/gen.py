@@ -237,6 +237,14 @@ def make_chunked_prefill(num_seqs: int, Hq: int, Hkv: int, d: int, *, page_size:
                 scale=cache["scale"], dtype="bf16", mask="causal", window=0)
 
 
+def make_backward(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, *, seed: int = 0, **kw) -> dict:
+    """A prefill problem plus the gradient flowing into its output: dO with
+    q's shape, standard normal, from stream 5 (bf16 bits like q)."""
+    c = make_prefill(B, Hq, Hkv, Nq, Nk, d, seed=seed, **kw)
+    c["do"] = _draw(seed, 5, (B, Hq, Nq, d), c["dtype"])
+    return c
+
+
 def prefill_config(name: str, seed: int = 0) -> dict:
     c = dict(CONFIGS[name])
     assert c.pop("kind") == "prefill"
