@@ -52,6 +52,16 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 PREFILL_CONFIG = "c2_causal_b4h16n2048"
 DECODE_CONFIG = "c5_paged_decode_64"
 CHUNKED_CONFIG = "c6_chunked_prefill_16"
+# every kernel the counter and clock summaries cover, with the workload it runs in bench.py
+KERNEL_WORKLOADS = {
+    "prefill_bf16_kernel<128, false>": PREFILL_CONFIG,
+    "decode_split_kernel<128>": DECODE_CONFIG,
+    "decode_combine_kernel<128>": DECODE_CONFIG,
+    "paged_prefill_bf16_kernel<128, false>": CHUNKED_CONFIG,
+    "bwd_prep_kernel": "backward of " + PREFILL_CONFIG,
+    "bwd_dq_kernel": "backward of " + PREFILL_CONFIG,
+    "bwd_dkdv_kernel": "backward of " + PREFILL_CONFIG,
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "sclk_prefill_c2_decode_c5.json")
 NUM_XCD = 8                   # GRBM_GUI_ACTIVE is counted once per accelerator die
@@ -279,7 +289,7 @@ def main() -> int:
     tflops = flops / (pre_mean * 1e-3) / 1e12
     dbytes = decode_bytes(dc)
     gbs = dbytes / (dec_mean * 1e-3) / 1e9
-    pkey = f"prefill_bf16_kernel<{pc['d']}>"
+    pkey = f"prefill_bf16_kernel<{pc['d']}, false>"
     ptraffic = measured_traffic(pkey, args.prefill_config)
     dtraffic = measured_traffic("decode_split_kernel<128>", DECODE_CONFIG)
 
@@ -398,7 +408,7 @@ def time_chunked(K: int, W: int) -> dict:
             "us": round(us, 2), "flop_per_call": flops,
             "workload": f"{CHUNKED_CONFIG} ({c['num_seqs']} seqs, Hq{c['Hq']} Hkv{c['Hkv']} d{c['d']}, "
                         f"{int(c['q_offsets'][-1])} chunk tokens over {int(c['seq_lens'].sum())} cached, causal)",
-            "kernel": f"paged_prefill_bf16_kernel<{c['d']}>"}
+            "kernel": f"paged_prefill_bf16_kernel<{c['d']}, false>"}
 
 
 # ------------------------------------------------------- counter summaries
@@ -445,14 +455,12 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
            "kernels": {}}
     for name in fetch:
         short = None
-        for tag in ("prefill_bf16_kernel<128>", "prefill_bf16_kernel<64>", "decode_split_kernel<128>",
-                    "decode_combine_kernel<128>", "paged_prefill_bf16_kernel<128>"):
-            if tag in name and (short is None or len(tag) > len(short)):
+        for tag in KERNEL_WORKLOADS:
+            if f"::{tag}" in name and (short is None or len(tag) > len(short)):
                 short = tag
         if short is None:
             continue
-        wl = (CHUNKED_CONFIG if short.startswith("paged") else
-              PREFILL_CONFIG if short.startswith("prefill") else DECODE_CONFIG)
+        wl = KERNEL_WORKLOADS[short]
         fk = float(np.mean(fetch[name]))
         wk = float(np.mean(write.get(name, [0.0])))
         out["kernels"][short] = {"workload": wl, "dispatches": len(fetch[name]), "fetch_kib_raw": fk,
@@ -488,17 +496,15 @@ def summarize_clock(d: str) -> int:
         for row in csv.DictReader(open(f)):
             if row.get("Counter_Name") == "GRBM_GUI_ACTIVE":
                 cyc[row["Dispatch_Id"]] = cyc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    flops = {"prefill_bf16_kernel<128>": prefill_flops(workloads.prefill_config(PREFILL_CONFIG)),
-             "paged_prefill_bf16_kernel<128>": chunked_flops(workloads.chunked_config(CHUNKED_CONFIG))}
+    flops = {"prefill_bf16_kernel<128, false>": prefill_flops(workloads.prefill_config(PREFILL_CONFIG)),
+             "paged_prefill_bf16_kernel<128, false>": chunked_flops(workloads.chunked_config(CHUNKED_CONFIG))}
     out = {"source_sha256": source_digest(),
            "command": "rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE -f csv -d <dir> -o run -- "
                       "python3 bench.py --pmc-pass ; python3 bench.py --summarize-clock <dir>",
            "kernels": {}}
-    # the combine kernel (~14 us) is too short for the per-die busy counter to
-    # bracket it reliably; only the two long kernels are summarised
-    workload = {"prefill_bf16_kernel<128>": PREFILL_CONFIG, "decode_split_kernel<128>": DECODE_CONFIG,
-                "paged_prefill_bf16_kernel<128>": CHUNKED_CONFIG}
-    for tag, wl in workload.items():
+    for tag, wl in KERNEL_WORKLOADS.items():
+        if tag == "decode_combine_kernel<128>":
+            continue   # ~14 us: too short for the per-die busy counter to bracket reliably
         # kernel names are demangled signatures: match the name, not a prefix of another
         ids = [i for i in dur if f"::{tag}(" in name[i] and i in cyc]
         if not ids:
