@@ -45,51 +45,21 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-constexpr int kRing = 4;   // pages each wave keeps in flight (its own LDS ring)
-
-// One page (16 tokens x d of one KV head) copied HBM -> LDS into a ring slot
-// with buffer_load_dwordx4 ... lds, 1 KiB per instruction.  The buffer covers
-// only the page's valid tokens, so slots past the sequence end read as zero
-// (whatever they hold in memory, NaN included).  voff[j] is this lane's source
-// offset for instruction j; it decides where each 16-byte chunk lands.
-template <int D>
-__device__ __forceinline__ void load_page(const uint16_t* page, int valid_tokens, uint8_t* slot,
-                                          const uint32_t (&voff)[D / 32]) {
-    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, valid_tokens * D * 2,
-                                                                  0x00020000);
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + j * 1024), 16, voff[j], 0, 0, 0);
-}
-
-// Wait until at most N of this wave's direct copies are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
+constexpr int kRing = 4;   // pages each wave keeps in flight (registers)
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int T = kSplitTokens;
-    constexpr int NM = D / 32;              // MFMA steps over the head dim = 1 KiB copies per page
+    constexpr int NM = D / 32;              // MFMA steps over the head dim = 16-byte loads per lane per page
     constexpr int CL = D / 8;               // lanes covering one token row with 16-byte reads
-    constexpr int TPI = 64 / CL;            // tokens per wave-wide read
-    constexpr int IT = kPage / TPI;         // reads per lane per V page
-    constexpr int PAGE_BYTES = kPage * D * 2;
+    constexpr int TPI = 64 / CL;            // tokens per wave-wide V read
+    constexpr int IT = kPage / TPI;         // V reads per lane per page
+    static_assert(IT == NM, "a K page and a V page take the same loads per lane");
     constexpr int WP = T / kPage / 4;       // pages per wave in a full split
-    // ring slot k of wave w is slot<k>[w]: one array per slot index, so each
-    // read names the slot whose copy it waits for
-    __shared__ __attribute__((aligned(1024))) uint8_t slot0[4][PAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t slot1[4][PAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t slot2[4][PAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t slot3[4][PAGE_BYTES];
-    static_assert(kRing == 4, "one array per ring slot");
+    static_assert(WP % kRing == 0, "V page i must land in ring slot i % kRing");
     __shared__ __attribute__((aligned(16))) float sc[4][T / 4][4];      // per wave: its tokens x 4 heads
+    __shared__ __attribute__((aligned(16))) float red_o[4][4][D];       // per wave: partial output of 4 heads
     __shared__ float red_m[4][4], red_l[4][4];
-    // each wave's partial output [4 heads][D] reuses its own slot 0 once its
-    // last page has been read
-    auto red_o = [&](int w) { return (float(*)[D])slot0[w]; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,40 +73,37 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int ntok = min(T, len - tok0);
     const int npages = (ntok + kPage - 1) / kPage;
     const int page0 = tok0 / kPage;
-    // physical page of logical page page0 + i sits in lane i (i < npages <= 32)
+    // physical page of logical page page0 + i sits in lane i (i < npages <= 64)
+    static_assert(T / kPage <= 64, "one block-table entry per lane");
     const int bt_lane = lane < npages ? p.block_table[(size_t)s * p.max_pages + page0 + lane] : 0;
     const size_t head_stride = (size_t)kPage * D;             // elements per (page, kv head)
     // this wave takes pages wave, wave + 4, ...
-    const int my_pages = npages > wave ? (npages - wave + 3) / 4 : 0;
+    const int n = npages > wave ? (npages - wave + 3) / 4 : 0;
     float (*scw)[4] = sc[wave];
-    // slot k of this wave's ring, resolved at compile time for constant k
-#define XATTN_SLOT(k) ((k) % kRing == 0 ? slot0[wave] : (k) % kRing == 1 ? slot1[wave] : (k) % kRing == 2 ? slot2[wave] : slot3[wave])
 
-    // Copy offsets.  K pages are XOR-swizzled by token row (16-byte chunk c of
-    // row r sits at chunk c ^ r), so the MFMA operand reads of 16 rows at one
-    // chunk hit 16 different banks; V pages stay row-major (their reads take
-    // whole rows).
+    // Pages go straight from HBM into registers.  Per lane and page: NM
+    // 16-byte loads.  A K page is loaded in the MFMA B-operand layout (token
+    // lane % 16, head-dim elements m*32 + (lane / 16)*8 ..+8), a V page as
+    // row pieces (token it*TPI + lane / CL, elements (lane % CL)*8 ..+8).
+    // Each page's buffer covers only its valid tokens, so slots past the
+    // sequence end read as zero whatever they hold (NaN included).
     uint32_t koff[NM], voff[NM];
 #pragma unroll
-    for (int j = 0; j < NM; ++j) {
-        const int r = j * (1024 / (D * 2)) + lane / CL;
-        const int pc = lane % CL;
-        koff[j] = (uint32_t)(r * D * 2 + ((pc ^ (r % CL)) << 4));
-        voff[j] = (uint32_t)(r * D * 2 + (pc << 4));
-    }
-    // MFMA operand reads of a K page: row (lane & 15), logical chunk m * 4 + (lane >> 4)
-    int kread[NM];
-#pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const int r = lane & 15, c = m * 4 + (lane >> 4);
-        kread[m] = r * D * 2 + ((c ^ (r % CL)) << 4);
+        koff[m] = (uint32_t)((lane & 15) * D * 2 + m * 64 + (lane >> 4) * 16);
+        voff[m] = (uint32_t)((m * TPI + lane / CL) * D * 2 + (lane % CL) * 16);
     }
-
-    auto page_ptr = [&](const uint16_t* base, int i) {
+    auto load_page = [&](u32x4 (&buf)[NM], const uint16_t* base, int i, const uint32_t (&off)[NM]) {
         const int phys = __builtin_amdgcn_readlane(bt_lane, wave + 4 * i);
-        return base + ((size_t)phys * p.Hkv + hkv) * head_stride;
+        const uint16_t* pg = base + ((size_t)phys * p.Hkv + hkv) * head_stride;
+        const int valid = min(kPage, ntok - (wave + 4 * i) * kPage);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pg, (short)0, valid * D * 2,
+                                                                            0x00020000);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) buf[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[m], 0, 0);
     };
-    auto page_valid = [&](int i) { return min(kPage, ntok - (wave + 4 * i) * kPage); };
+    // the ring: kRing pages of registers, slot k always named by a constant
+    u32x4 ring[kRing][NM];
 
     for (int hc = 0; hc < p.group; hc += 4) {
         // ---- 1. scores: Q' K^T, four heads replicated over the 16 MFMA rows
@@ -151,28 +118,30 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 qa[m] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // q landed before the ring copies start counting
-#pragma unroll
-        for (int i = 0; i < kRing; ++i)
-            if (i < my_pages) load_page<D>(page_ptr(p.kp, i), page_valid(i), XATTN_SLOT(i), koff);
+        // In a full split (n = WP) the wave's loads form one stream: its K
+        // pages 0 .. WP-1, then its V pages 0 .. WP-1, stream page j in slot
+        // j % kRing, each slot reloaded with page j + kRing right after page j
+        // is used, so the first V pages are in flight while the last K pages
+        // are scored and while the softmax runs.  A shorter (last) split loads
+        // its V pages after its K pages.
+        const bool full_split = n == WP;
+        static_for<kRing>([&](auto k_tag) {
+            constexpr int k = decltype(k_tag)::value;
+            if (k < n) load_page(ring[k], p.kp, k, koff);
+        });
         float mloc[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-        // One K page: wait for its copy, scores on the matrix cores, refill
-        // the slot with the page kRing ahead, park the scores.  FULL (all WP
-        // pages present) lets every wait count be a constant.
         auto k_page = [&](auto full_tag, auto i_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
             constexpr int i = decltype(i_tag)::value;
-            if (FULL) wait_vm<(WP - 1 - i < kRing - 1 ? WP - 1 - i : kRing - 1) * NM>();
-            else wait_vm<0>();
             f32x4 acc = f32x4{};
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const u32x4 w = *(const u32x4*)(XATTN_SLOT(i) + kread[m]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);
-            }
-            if (i + kRing < my_pages) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this slot's reads retired
-                load_page<D>(page_ptr(p.kp, i + kRing), page_valid(i + kRing), XATTN_SLOT(i), koff);
+            for (int m = 0; m < NM; ++m)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], __builtin_bit_cast(bf16x8, ring[i % kRing][m]), acc,
+                                                              0, 0, 0);
+            if (i + kRing < WP) {
+                if (FULL || i + kRing < n) load_page(ring[i % kRing], p.kp, i + kRing, koff);
+            } else if (FULL) {
+                load_page(ring[i % kRing], p.vp, i + kRing - WP, voff);
             }
             const int t_in = (wave + 4 * i) * kPage + (lane & 15);
             if (lane < 16) {
@@ -184,24 +153,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 for (int r = 0; r < 4; ++r) mloc[r] = fmaxf(mloc[r], v[r]);
             }
         };
-        if (my_pages == WP) {
+        if (full_split) {
             static_for<WP>([&](auto i_tag) { k_page(std::true_type{}, i_tag); });
         } else {
             static_for<WP>([&](auto i_tag) {
-                if (decltype(i_tag)::value < my_pages) k_page(std::false_type{}, i_tag);
+                if (decltype(i_tag)::value < n) k_page(std::false_type{}, i_tag);
+            });
+            static_for<kRing>([&](auto k_tag) {
+                constexpr int k = decltype(k_tag)::value;
+                if (k < n) load_page(ring[k], p.vp, k, voff);
             });
         }
-        // V copies start now and land during the softmax
-#pragma unroll
-        for (int i = 0; i < kRing; ++i)
-            if (i < my_pages) load_page<D>(page_ptr(p.vp, i), page_valid(i), XATTN_SLOT(i), voff);
         // ---- 2. this wave's own max and sum over its tokens
         float sm[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) mloc[r] = wave_max(mloc[r]);
         {
             f32x4 part = f32x4{};
-            for (int t = lane; t < my_pages * kPage; t += 64) {
+            for (int t = lane; t < n * kPage; t += 64) {
                 f32x4 v = *(const f32x4*)(&scw[t][0]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -219,19 +188,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
-        auto v_page = [&](auto full_tag, auto i_tag) {
-            constexpr bool FULL = decltype(full_tag)::value;
+        auto v_page = [&](auto i_tag) {
             constexpr int i = decltype(i_tag)::value;
-            if (FULL) wait_vm<(WP - 1 - i < kRing - 1 ? WP - 1 - i : kRing - 1) * NM>();
-            else wait_vm<0>();
             u32x4 vv[IT];
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
-                vv[it] = *(const u32x4*)(XATTN_SLOT(i) + (it * TPI + lane / CL) * D * 2 + (lane % CL) * 16);
-            if (i + kRing < my_pages) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);
-                load_page<D>(page_ptr(p.vp, i + kRing), page_valid(i + kRing), XATTN_SLOT(i), voff);
-            }
+            for (int it = 0; it < IT; ++it) vv[it] = ring[i % kRing][it];
+            if (i + kRing < WP && i + kRing < n) load_page(ring[i % kRing], p.vp, i + kRing, voff);
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 // weights of slots past the end are 0 (their scores were -inf) and their values 0
@@ -247,13 +209,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 }
             }
         };
-        if (my_pages == WP) {
-            static_for<WP>([&](auto i_tag) { v_page(std::true_type{}, i_tag); });
-        } else {
-            static_for<WP>([&](auto i_tag) {
-                if (decltype(i_tag)::value < my_pages) v_page(std::false_type{}, i_tag);
-            });
-        }
+        static_for<WP>([&](auto i_tag) {
+            if (decltype(i_tag)::value < n) v_page(i_tag);
+        });
         // reduce over the lanes that hold other tokens of the same columns
 #pragma unroll
         for (int off = CL; off < 64; off <<= 1)
@@ -261,12 +219,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) oacc[r][e] += __shfl_xor(oacc[r][e], off);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's ring reads retired
         if (lane < CL) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                *(f32x4*)(&red_o(wave)[r][lane * 8]) = f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
-                *(f32x4*)(&red_o(wave)[r][lane * 8 + 4]) = f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
+                *(f32x4*)(&red_o[wave][r][lane * 8]) = f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
+                *(f32x4*)(&red_o[wave][r][lane * 8 + 4]) = f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
             }
         }
         if (lane == 0) {
@@ -289,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const float sc_w = red_m[w][r] == neg_inf() ? 0.f : fast_exp2(red_m[w][r] - M);
-                    num = __builtin_fmaf(sc_w, red_o(w)[r][c], num);
+                    num = __builtin_fmaf(sc_w, red_o[w][r][c], num);
                     den = __builtin_fmaf(sc_w, red_l[w][r], den);
                 }
                 const size_t row = ((size_t)s * p.Hq + hkv * p.group + hl) * p.max_splits + split;
@@ -297,9 +254,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 if (c == 0) p.ws_lse[row] = M + fast_log2(den);
             }
         }
-        __syncthreads();  // sc / red / ring reused by the next head chunk
+        __syncthreads();  // sc / red reused by the next head chunk
     }
-#undef XATTN_SLOT
 }
 
 // One wave per (sequence, query head): O = sum_s w_s o_s / sum_s w_s with

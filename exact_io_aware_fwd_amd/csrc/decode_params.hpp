@@ -7,7 +7,7 @@
 
 namespace xattn {
 
-constexpr int kSplitTokens = 512;  // keys per split of one (sequence, KV head)
+constexpr int kSplitTokens = 1024;  // keys per split of one (sequence, KV head)
 constexpr int kPage = 16;          // tokens per KV page
 
 struct DecodeParams {
