@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) float sc[4][T / 4][4];      // per wave: its tokens x 4 heads
     __shared__ __attribute__((aligned(16))) float red_o[4][4][D];       // per wave: partial output of 4 heads
     __shared__ float red_m[4][4], red_l[4][4];
+    __shared__ __attribute__((aligned(16))) uint8_t kst[4][2][kPage * D * 2];  // per wave: two K page stages
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -81,17 +82,27 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int n = npages > wave ? (npages - wave + 3) / 4 : 0;
     float (*scw)[4] = sc[wave];
 
-    // Pages go straight from HBM into registers.  Per lane and page: NM
-    // 16-byte loads.  A K page is loaded in the MFMA B-operand layout (token
-    // lane % 16, head-dim elements m*32 + (lane / 16)*8 ..+8), a V page as
-    // row pieces (token it*TPI + lane / CL, elements (lane % CL)*8 ..+8).
-    // Each page's buffer covers only its valid tokens, so slots past the
-    // sequence end read as zero whatever they hold (NaN included).
-    uint32_t koff[NM], voff[NM];
+    // Pages go straight from HBM into registers, NM 16-byte loads per lane
+    // and page, each load a contiguous 1 KiB of the page (token m*TPI +
+    // lane / CL, elements (lane % CL)*8 ..+8): a row-major V page is then
+    // ready for the P V products, and a K page goes through the wave's LDS
+    // stage into the matrix-core operand layout (operand loads that take a
+    // 64-byte piece of 16 rows each stream about 14 % slower from HBM).  Each
+    // page's buffer covers only its valid tokens, so slots past the sequence
+    // end read as zero whatever they hold (NaN included).
+    uint32_t voff[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) voff[m] = (uint32_t)((m * TPI + lane / CL) * D * 2 + (lane % CL) * 16);
+    // K stage: 16-byte chunk c of token row r sits at chunk c ^ (r % CL), so
+    // the stores of whole rows and the operand reads of 16 rows at one chunk
+    // both hit distinct banks
+    int kput[NM], kget[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        koff[m] = (uint32_t)((lane & 15) * D * 2 + m * 64 + (lane >> 4) * 16);
-        voff[m] = (uint32_t)((m * TPI + lane / CL) * D * 2 + (lane % CL) * 16);
+        const int rw = m * TPI + lane / CL, cw = lane % CL;
+        kput[m] = rw * D * 2 + ((cw ^ (rw % CL)) << 4);
+        const int rr = lane & 15, cr = m * 4 + (lane >> 4);
+        kget[m] = rr * D * 2 + ((cr ^ (rr % CL)) << 4);
     }
     auto load_page = [&](u32x4 (&buf)[NM], const uint16_t* base, int i, const uint32_t (&off)[NM]) {
         const int phys = __builtin_amdgcn_readlane(bt_lane, wave + 4 * i);
@@ -127,19 +138,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         const bool full_split = n == WP;
         static_for<kRing>([&](auto k_tag) {
             constexpr int k = decltype(k_tag)::value;
-            if (k < n) load_page(ring[k], p.kp, k, koff);
+            if (k < n) load_page(ring[k], p.kp, k, voff);
         });
         float mloc[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
         auto k_page = [&](auto full_tag, auto i_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
             constexpr int i = decltype(i_tag)::value;
+            uint8_t* stage = kst[wave][i & 1];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) *(u32x4*)(stage + kput[m]) = ring[i % kRing][m];
             f32x4 acc = f32x4{};
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], __builtin_bit_cast(bf16x8, ring[i % kRing][m]), acc,
-                                                              0, 0, 0);
+            for (int m = 0; m < NM; ++m) {
+                const u32x4 w = *(const u32x4*)(stage + kget[m]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);
+            }
             if (i + kRing < WP) {
-                if (FULL || i + kRing < n) load_page(ring[i % kRing], p.kp, i + kRing, koff);
+                if (FULL || i + kRing < n) load_page(ring[i % kRing], p.kp, i + kRing, voff);
             } else if (FULL) {
                 load_page(ring[i % kRing], p.vp, i + kRing - WP, voff);
             }
