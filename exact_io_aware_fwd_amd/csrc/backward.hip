@@ -51,6 +51,21 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tl, int kb, int cb) 
     return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
+// Order a product's LDS operand reads AHEAD MFMAs ahead of their use (R
+// reads per MFMA), as the forward's tile step does.
+template <int NMFMA, int R, int AHEAD>
+__device__ __forceinline__ void order_operand_reads() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);
+#pragma unroll
+    for (int i = 0; i < NMFMA - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+#endif
+}
+
 // acc[jb] = sum_kk A(rows of the tile) x bf[kk]: a 64 x 32 product over the
 // head dim (16 MFMAs).
 __device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)[kBD / 16], f32x16 (&acc)[2]) {
@@ -61,6 +76,7 @@ __device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
             acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(rl, jb, kk), bf[kk], acc[jb], 0, 0, 0);
+    order_operand_reads<kBD / 8, 1, 4>();
 }
 
 // acc[cb] += sum_kb A(transposed tile) x pf[kb]: a (d x 64) by (64 x 32)
@@ -71,6 +87,7 @@ __device__ __forceinline__ void tr_times(const uint8_t* tl, const bf16x8 (&pf)[4
 #pragma unroll
         for (int cb = 0; cb < kBD / 32; ++cb)
             acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(tl, kb, cb), pf[kb], acc[cb], 0, 0, 0);
+    order_operand_reads<kBD / 8, 2, 2>();
 }
 
 // A 64 x 32 accumulator pair as the bf16 B operand of the next product, one

@@ -40,6 +40,25 @@ struct PrefillBf16State {
     float l_f32;   // same sum over the unrounded fp32 weights: gives the LSE
 };
 
+// Order one product's LDS operand reads against its MFMAs: the first
+// AHEAD * R reads, then each MFMA followed by the next R reads, then the last
+// AHEAD MFMAs.  Left to itself the compiler issues each operand read about
+// two MFMAs ahead, and its latency then shows between the MFMAs; holding the
+// reads this far ahead (AHEAD 4 for K, 2 for V^T, measured) cut the causal
+// prefill's cycles by 5-6 %.
+template <int NMFMA, int R, int AHEAD>
+__device__ __forceinline__ void order_reads_ahead() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);   // DS reads
+#pragma unroll
+    for (int i = 0; i < NMFMA - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+#endif
+}
+
 // S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
 // key tile resident in LDS.  kl / vl point at this lane's own base in the
 // K / V tile; every other operand address is a compile-time offset from it.
@@ -58,6 +77,7 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
             const u32x4 a = *(const u32x4*)(kl + jb * 32 * C::KS * 16 + kk * 32);
             s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), st.qf[kk], s[jb], 0, 0, 0);
         }
+    order_reads_ahead<2 * C::DK, 1, 4>();
     // ---- mask, only where the tile is not fully visible to this wave
     if (!full) {
 #pragma unroll
@@ -139,6 +159,7 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
             const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
             st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kb], st.acc[cb], 0, 0, 0);
         }
+    order_reads_ahead<4 * C::CB, 2, 2>();
 }
 
 // SINKS: the window mask keeps sink tokens visible (the second key interval);
