@@ -82,6 +82,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.doc_offsets = mask.kind == ATTN_MASK_DOCUMENT ? mask.doc_offsets : nullptr;
     p.num_docs = mask.kind == ATTN_MASK_DOCUMENT ? mask.num_docs : 0;
     p.num_q_tiles = (int)tiles;
+    p.q_tile_pairs = 0;
     p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
     p.sink_logits = mask.sink_logits;
 

@@ -36,6 +36,7 @@ struct PrefillParams {
     const int32_t* doc_offsets;
     int num_docs;
     int num_q_tiles;
+    int q_tile_pairs;          // > 0: workgroup u takes query tiles num_q_tiles-1-u and u (set by the launcher)
     int sink_end;              // window mask: keys [0, sink_end) stay visible too (0: none)
     const float* sink_logits;  // [Hq] learned sink logit per query head, or null
 };

@@ -177,106 +177,118 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, lets loads use scalar control
     const int nbk = p.B * p.Hkv;
-    int bk, qt, g;
-    decode_work(blockIdx.x, nbk, p.num_q_tiles, p.group, bk, qt, g);
+    int bk, unit, g;
+    decode_work(blockIdx.x, nbk, p.q_tile_pairs > 0 ? p.q_tile_pairs : p.num_q_tiles, p.group, bk, unit, g);
     const int b = bk / p.Hkv, hkv = bk % p.Hkv, hq = hkv * p.group + g;
 
     const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
     const uint16_t* __restrict__ kg_ = (const uint16_t*)p.k + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
     const uint16_t* __restrict__ vg_ = (const uint16_t*)p.v + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
 
-    const int r0 = qt * C::BM;
-    const int r_last = min(r0 + C::BM, p.Nq) - 1;
-    const int w0 = r0 + wave * 32;                      // first row of this wave
-    const int w_last = min(w0 + 31, p.Nq - 1);          // last valid row of this wave
-    const int row = w0 + (lane & 31);
-    const bool row_ok = row < p.Nq;
+    // Under a causal mask a row tile's work grows with its index.  A
+    // workgroup then takes two row tiles, a heavy one and its mirror (tiles
+    // num_q_tiles-1-u and u), so every workgroup does about the same work and
+    // the grid drains evenly instead of ending on a round of light tiles.
+    // Pairs go in ascending u, so an odd middle tile (alone) comes last.
+    const bool paired = p.q_tile_pairs > 0;
+    const int u = paired ? p.q_tile_pairs - 1 - unit : unit;
+    const int nsub = paired && p.num_q_tiles - 1 - u != u ? 2 : 1;
+    for (int sub = 0; sub < nsub; ++sub) {
+        const int qt = paired && sub == 0 ? p.num_q_tiles - 1 - u : u;
+        if (sub > 0) __syncthreads();   // every wave is done with the ring before it is refilled
+        const int r0 = qt * C::BM;
+        const int r_last = min(r0 + C::BM, p.Nq) - 1;
+        const int w0 = r0 + wave * 32;                      // first row of this wave
+        const int w_last = min(w0 + 31, p.Nq - 1);          // last valid row of this wave
+        const int row = w0 + (lane & 31);
+        const bool row_ok = row < p.Nq;
 
-    int lo_i, hi_i;
-    row_interval(p, row, lo_i, hi_i);
-    int lo_wg, tmp, hi_wg;
-    row_interval(p, r0, lo_wg, tmp);
-    row_interval(p, r_last, tmp, hi_wg);
-    int lo_w_first, hi_w_first, lo_w_last, hi_w_last;
-    row_interval(p, w0, lo_w_first, hi_w_first);
-    row_interval(p, w_last, lo_w_last, hi_w_last);
-    const bool wave_has_rows = w0 < p.Nq;
+        int lo_i, hi_i;
+        row_interval(p, row, lo_i, hi_i);
+        int lo_wg, tmp, hi_wg;
+        row_interval(p, r0, lo_wg, tmp);
+        row_interval(p, r_last, tmp, hi_wg);
+        int lo_w_first, hi_w_first, lo_w_last, hi_w_last;
+        row_interval(p, w0, lo_w_first, hi_w_first);
+        row_interval(p, w_last, lo_w_last, hi_w_last);
+        const bool wave_has_rows = w0 < p.Nq;
 
-    PrefillBf16State<D> st;
-    // Q fragment: MFMA B operand, column = query row (lane & 31), k slots
-    // (lane >> 5) * 8 .. +8 of every 16-wide step of the head dim.
-    {
-        const uint16_t* qrow = qg + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + (row_ok ? row : 0)) * D;
-#pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) {
-            u32x4 w = row_ok ? *(const u32x4*)(qrow + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
-            st.qf[kk] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
-    st.m_run = neg_inf();   // running row max, base-2 scaled units
-    st.l_run = 0.f;
-    st.l_f32 = 0.f;
-
-    const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
-
-    uint32_t koff[C::KLW], voff[C::VLW];
-    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
-    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
-    // this lane's operand bases inside a K / V tile
-    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
-    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-
-    // One stage of the ring: wait for this tile's copies, make them visible to
-    // every wave (which also proves every wave is done with the other stage),
-    // start copying the next tile into the other stage, then compute.
-    // Iteration it runs tile tile_of(tr, it).
-    auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
-        __syncthreads();
-        if (it + 1 < tr.n) {
-            const int tn = tile_of(tr, it + 1);
-            load_tile_async<D, C::KS, C::KLOADS>(kg_, tn * C::BN, p.Nk, kn, koff, wave);
-            load_tile_async<D, C::VS, C::VLOADS>(vg_, tn * C::BN, p.Nk, vn, voff, wave);
-        }
-        const int n0 = tile_of(tr, it) * C::BN;
-        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
-        if (active) {
-            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
-        }
-    };
-
-    if (tr.n > 0) {
-        const int t0 = tile_of(tr, 0);
-        load_tile_async<D, C::KS, C::KLOADS>(kg_, t0 * C::BN, p.Nk, k_lds0, koff, wave);
-        load_tile_async<D, C::VS, C::VLOADS>(vg_, t0 * C::BN, p.Nk, v_lds0, voff, wave);
-        for (int it = 0; it < tr.n; it += 2) {
-            stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
-            if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-        }
-    }
-    f32x16* acc = st.acc;
-    const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
-
-    // ---- epilogue: O = acc / l once, LSE in natural log (with the sink, if any)
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    if (row_ok) {
-        const float s2 = p.sink_logits != nullptr ? p.sink_logits[hq] * kLog2e : neg_inf();
-        float inv, lse_row;
-        finish_row(st.m_run, l_tot, lf_tot, s2, inv, lse_row);
-        uint16_t* orow = (uint16_t*)p.o + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + row) * D;
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[cb][4 * gq + 0] * inv, acc[cb][4 * gq + 1] * inv);
-                w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
-                *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
+        PrefillBf16State<D> st;
+        // Q fragment: MFMA B operand, column = query row (lane & 31), k slots
+        // (lane >> 5) * 8 .. +8 of every 16-wide step of the head dim.
+        {
+            const uint16_t* qrow = qg + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + (row_ok ? row : 0)) * D;
+    #pragma unroll
+            for (int kk = 0; kk < C::DK; ++kk) {
+                u32x4 w = row_ok ? *(const u32x4*)(qrow + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+                st.qf[kk] = __builtin_bit_cast(bf16x8, w);
             }
-        if (p.lse != nullptr && lane < 32) p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = lse_row;
+        }
+    #pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
+        st.m_run = neg_inf();   // running row max, base-2 scaled units
+        st.l_run = 0.f;
+        st.l_f32 = 0.f;
+
+        const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
+
+        uint32_t koff[C::KLW], voff[C::VLW];
+        tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+        tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
+        // this lane's operand bases inside a K / V tile
+        const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+        const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+
+        // One stage of the ring: wait for this tile's copies, make them visible to
+        // every wave (which also proves every wave is done with the other stage),
+        // start copying the next tile into the other stage, then compute.
+        // Iteration it runs tile tile_of(tr, it).
+        auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
+            __syncthreads();
+            if (it + 1 < tr.n) {
+                const int tn = tile_of(tr, it + 1);
+                load_tile_async<D, C::KS, C::KLOADS>(kg_, tn * C::BN, p.Nk, kn, koff, wave);
+                load_tile_async<D, C::VS, C::VLOADS>(vg_, tn * C::BN, p.Nk, vn, voff, wave);
+            }
+            const int n0 = tile_of(tr, it) * C::BN;
+            const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
+            if (active) {
+                const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
+                tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
+            }
+        };
+
+        if (tr.n > 0) {
+            const int t0 = tile_of(tr, 0);
+            load_tile_async<D, C::KS, C::KLOADS>(kg_, t0 * C::BN, p.Nk, k_lds0, koff, wave);
+            load_tile_async<D, C::VS, C::VLOADS>(vg_, t0 * C::BN, p.Nk, v_lds0, voff, wave);
+            for (int it = 0; it < tr.n; it += 2) {
+                stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
+                if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+            }
+        }
+        f32x16* acc = st.acc;
+        const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
+
+        // ---- epilogue: O = acc / l once, LSE in natural log (with the sink, if any)
+        const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+        if (row_ok) {
+            const float s2 = p.sink_logits != nullptr ? p.sink_logits[hq] * kLog2e : neg_inf();
+            float inv, lse_row;
+            finish_row(st.m_run, l_tot, lf_tot, s2, inv, lse_row);
+            uint16_t* orow = (uint16_t*)p.o + (((size_t)b * p.Hq + hq) * (size_t)p.Nq + row) * D;
+    #pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+    #pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[cb][4 * gq + 0] * inv, acc[cb][4 * gq + 1] * inv);
+                    w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv);
+                    *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
+                }
+            if (p.lse != nullptr && lane < 32) p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = lse_row;
+        }
     }
 }
 
@@ -354,6 +366,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     p.doc_offsets = nullptr;
     p.num_docs = 0;
     p.sink_end = sink_end;
+    p.q_tile_pairs = 0;
 
     const int r_last = min(r0 + C::BM, nq) - 1;
     const int w0 = r0 + wave * 32;
@@ -486,8 +499,30 @@ int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t st
 
 int prefill_bf16_rows_per_block() { return PrefillBf16Cfg<128>::BM; }
 
-int launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
-    const int blocks = p.B * p.Hq * p.num_q_tiles;
+// Compute units of the current device (read once per process).
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            return 256;
+    }
+    return cus;
+}
+
+int launch_prefill_bf16(const PrefillParams& p0, int d, hipStream_t stream) {
+    PrefillParams p = p0;
+    // Causal row tiles are paired (see the kernel) when the unpaired grid is
+    // at most two rounds of the workgroup slots (two per CU): with more rounds
+    // the heaviest-first order already drains the grid evenly, and measured
+    // pairing was then slower (C3a +6 % cycles; C2 -2 %).
+    const long long unpaired = (long long)p.B * p.Hq * p.num_q_tiles;
+    const bool pair = p.mask_kind == kMaskCausal && p.num_q_tiles > 1 && unpaired <= 2LL * 2 * device_cus();
+    p.q_tile_pairs = pair ? (p.num_q_tiles + 1) / 2 : 0;
+    const int blocks = p.B * p.Hq * (p.q_tile_pairs > 0 ? p.q_tile_pairs : p.num_q_tiles);
     const bool sinks = p.sink_end > 0;
     if (d == 128) {
         if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
