@@ -68,15 +68,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int rest = blockIdx.x / p.Hkv;
     const int split = rest % p.max_splits;
     const int s = rest / p.max_splits;
-    const int len = p.seq_lens[s];
     const int tok0 = split * T;
+    const int page0 = tok0 / kPage;
+    // Physical page of logical page page0 + i sits in lane i (i < npages <=
+    // 64).  The entries of a whole split are read together with the sequence
+    // length (indices clamped to the table row; entries past the sequence are
+    // never used), so the first page loads wait for one memory round trip,
+    // not two; the empty asm keeps the load ahead of the early exit.
+    static_assert(T / kPage <= 64, "one block-table entry per lane");
+    const int bt_lane = p.block_table[(size_t)s * p.max_pages + min(page0 + lane, p.max_pages - 1)];
+    const int len = p.seq_lens[s];
+    asm volatile("" ::"v"(bt_lane));
     if (tok0 >= len) return;
     const int ntok = min(T, len - tok0);
     const int npages = (ntok + kPage - 1) / kPage;
-    const int page0 = tok0 / kPage;
-    // physical page of logical page page0 + i sits in lane i (i < npages <= 64)
-    static_assert(T / kPage <= 64, "one block-table entry per lane");
-    const int bt_lane = lane < npages ? p.block_table[(size_t)s * p.max_pages + page0 + lane] : 0;
     const size_t head_stride = (size_t)kPage * D;             // elements per (page, kv head)
     // this wave takes pages wave, wave + 4, ...
     const int n = npages > wave ? (npages - wave + 3) / 4 : 0;
