@@ -47,6 +47,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kRing = 4;   // pages each wave keeps in flight (registers)
 
+// Cache policy of the page loads: nontemporal (the nt bit).  Every cache byte
+// is read once per decode step, and in a 4.5 GiB streaming test nontemporal
+// loads of shuffled 4 KiB pages ran at 6.44 TB/s against 5.98 TB/s with the
+// default policy.
+constexpr int kStreamLoad = 2;
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int T = kSplitTokens;
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pg, (short)0, valid * D * 2,
                                                                             0x00020000);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) buf[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[m], 0, 0);
+        for (int m = 0; m < NM; ++m) buf[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[m], 0, kStreamLoad);
     };
     // the ring: kRing pages of registers, slot k always named by a constant
     u32x4 ring[kRing][NM];
