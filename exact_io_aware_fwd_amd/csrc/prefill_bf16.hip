@@ -45,7 +45,8 @@ struct PrefillBf16State {
 // AHEAD MFMAs.  Left to itself the compiler issues each operand read about
 // two MFMAs ahead, and its latency then shows between the MFMAs; holding the
 // reads this far ahead (AHEAD 4 for K, 2 for V^T, measured) cut the causal
-// prefill's cycles by 5-6 %.
+// prefill's cycles by 5-6 %.  The V^T reads keep AHEAD 2 inside
+// interleave_weights_products below; the backward's products use this order.
 template <int NMFMA, int R, int AHEAD>
 __device__ __forceinline__ void order_reads_ahead() {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -57,6 +58,36 @@ __device__ __forceinline__ void order_reads_ahead() {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 #endif
+}
+
+// Order the weights-and-products part of a tile: the first V^T reads and the
+// first 16-key block's weights (PRE VALU ops: exponentials, sums and bf16
+// packing), then each MFMA followed by the next two V^T reads and VALU_PER
+// ops of the following blocks' weights, so the exponentials of block kb+1
+// issue while block kb's products run on the matrix core (measured: C2
+// causal prefill 189 K -> 184 K cycles, nothing else changed).
+template <int NMFMA, int PRE, int VALU_PER>
+__device__ __forceinline__ void interleave_weights_products() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);           // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, PRE, 0);         // VALU
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        if (i < NMFMA - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i < NMFMA - NMFMA / 4) __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+    }
+#endif
+}
+
+// (mask & a) | (~mask & b).  Written as one v_bfi_b32: the plain C form of
+// this select over the 32 scores of a lane was combined by the compiler into
+// three-input logic ops that read a neighbouring score's register (wrong
+// results, seen in the generated code of this kernel).
+__device__ __forceinline__ float bit_select(uint32_t mask, float a, float b) {
+    float out;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(out) : "v"(mask), "v"(a), "v"(b));
+    return out;
 }
 
 // S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
@@ -80,12 +111,26 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
     order_reads_ahead<2 * C::DK, 1, 4>();
     // ---- mask, only where the tile is not fully visible to this wave
     if (!full) {
+        // Score i = 16 jb + r of this lane is key base + c_i with the
+        // compile-time offset c_i = 8 (i / 4) + i % 4, increasing in i.  So
+        // each bound of the visible set (key <= hi_i; key >= lo_i or key <
+        // sink_end) keeps a run of consecutive i, counted by below(x) =
+        // #{i : c_i < x}, and the visible set is one 32-bit mask per lane.
+        const int base = n0 + 4 * (lane >> 5);
+        auto below = [](int x) {
+            x = min(max(x, 0), 64);
+            return 4 * (x >> 3) + min(x & 7, 4);
+        };
+        auto low_bits = [](int k) { return k >= 32 ? 0xffffffffu : (1u << k) - 1u; };
+        uint32_t vis = low_bits(below(hi_i - base + 1));
+        vis &= ~low_bits(below(lo_i - base)) | low_bits(below(sink_end - base));
+        const float ninf = neg_inf();
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (key > hi_i || (key < lo_i && key >= sink_end)) s[jb][r] = neg_inf();
+                const uint32_t keep = (uint32_t)((int)(vis << (31 - (16 * jb + r))) >> 31);   // bit i, sign-extended
+                s[jb][r] = bit_select(keep, s[jb][r], ninf);
             }
     }
     // Row max: each lane reduces its own half of the row (two independent
@@ -114,52 +159,47 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
         st.m_run = m_new;
     }
     const float m_use = st.m_run == neg_inf() ? 0.f : st.m_run;
+    // Weights, P^T operands and O^T += V^T P^T, one 16-key block kb at a time.
+    // O is normalised by the sum of the same bf16-rounded weights the PV
+    // product uses, so it is an exact weighted average of V rows under those
+    // weights (a dot with (1, 1) adds two packed bf16 values at once); the LSE
+    // uses the fp32 sum, free of the weights' rounding.
+    //
+    // The V^T operand comes from the row-major V tile through two transposing
+    // reads (ds_read_b64_tr_b16): in each 16-lane group, source lane 4k+q
+    // points at 4 columns c0+4q.. of key row k, and lane i receives column
+    // c0+i of those 4 rows.  Rows are picked so the 8 keys a lane holds are the
+    // ones its P^T operand slots hold.
     float fs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], scale_log2, -m_use));
-            fs[(r & 1) + 2 * jb] += s[jb][r];
-        }
-    const float fsum = (fs[0] + fs[1]) + (fs[2] + fs[3]);
-    // P^T operands (bf16), one per 16-key block.  O is normalised by the sum of
-    // the same bf16-rounded weights the PV product uses, so it is an exact
-    // weighted average of V rows under those weights (a dot with (1, 1) adds
-    // two packed bf16 values at once); the LSE uses the fp32 sum, free of the
-    // weights' rounding.
-    bf16x8 pf[4];
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int jb = kb >> 1, h = (kb & 1) * 8;
+#pragma unroll
+        for (int r = h; r < h + 8; ++r) {
+            s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], scale_log2, -m_use));
+            fs[(r & 1) + 2 * jb] += s[jb][r];
+        }
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             w[e] = pack_bf16x2(s[jb][h + 2 * e], s[jb][h + 2 * e + 1]);
             ps[e & 1] = sum_bf16x2(w[e], ps[e & 1]);
         }
-        pf[kb] = __builtin_bit_cast(bf16x8, w);
-    }
-    st.l_run += ps[0] + ps[1];
-    st.l_f32 += fsum;
-    // ---- O^T += V^T P^T.  The V^T operand comes from the row-major V tile
-    // through two transposing reads (ds_read_b64_tr_b16): in each 16-lane
-    // group, source lane 4k+q points at 4 columns c0+4q.. of key row k, and
-    // lane i receives column c0+i of those 4 rows.  Rows are picked so the 8
-    // keys a lane holds are the ones its P^T operand slots hold.
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int cb = 0; cb < C::CB; ++cb) {
             const uint8_t* vp = vl + kb * 16 * C::VS * 16 + cb * 64;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
             const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-            st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kb], st.acc[cb], 0, 0, 0);
+            st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf, st.acc[cb], 0, 0, 0);
         }
-    order_reads_ahead<4 * C::CB, 2, 2>();
+    }
+    st.l_run += ps[0] + ps[1];
+    st.l_f32 += (fs[0] + fs[1]) + (fs[2] + fs[3]);
+    interleave_weights_products<4 * C::CB, 40, 6>();
 }
 
 // SINKS: the window mask keeps sink tokens visible (the second key interval);
