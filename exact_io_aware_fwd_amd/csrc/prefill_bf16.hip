@@ -286,6 +286,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
         auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t landed
             __syncthreads();
+            // Two workgroups share each CU, and on a SIMD the older wave wins
+            // the issue arbitration when priorities tie.  With one round of
+            // workgroups (C2) the second-dispatched half then ran 35 % slower
+            // per tile and ended about 14 us after the first half (workgroup
+            // timestamps).  Handing the higher priority to the two halves in
+            // turn, tile by tile, evens them out: C2 181 K -> 174 K cycles.
+            if (((it + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
             if (it + 1 < tr.n) {
                 const int tn = tile_of(tr, it + 1);
                 load_tile_async<D, C::KS, C::KLOADS>(kg_, tn * C::BN, p.Nk, kn, koff, wave);
