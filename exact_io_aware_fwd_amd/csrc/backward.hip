@@ -10,7 +10,7 @@
 //   prep   per query row: -LSE log2(e), D, the row's visible key interval,
 //          and the learned sink's gradient -sum_i P_sink,i D_i;
 //   dQ     one workgroup per (batch, query head, 128-row query tile), each
-//          wave owning 32 rows as in the forward; per 64-key tile it
+//          wave owning 32 rows as in the forward; per 32-key tile it
 //          recomputes S^T = K Q^T and dP^T = V dO^T and accumulates
 //          dQ^T += K^T dS^T (the forward's O^T += V^T P^T with K and dS);
 //   dK/dV  one workgroup per (batch, KV head, 128-key tile), each wave owning
@@ -179,10 +179,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) {
     }
 }
 
-// dQ: per 64-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
+// dQ: per 32-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
 // dQ^T += K^T dS^T.  K is copied twice (row and transposed layouts), V once.
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardParams p) {
-    using C = PrefillBf16Cfg<kBD>;
+// With 32-key tiles a stage of that ring is 28 KiB and a wave needs 190
+// registers, so two workgroups share a CU and two waves each SIMD (64-key
+// tiles took 54 KiB per stage and 280 registers, one wave per SIMD; the
+// backward of C2 went from 468 to 414 us with this change).
+struct DqCfg {
+    static constexpr int BN = 32;
+    static constexpr int KS = kBD / 8 + 1;        // row layout: one 16-byte slot of padding per row
+    static constexpr int VS = kBD / 8 + 4;        // transposed layout: four slots
+    static constexpr int KLOADS = 9;              // 32 x 17 slots = 8.5 KiB, copied as 9 KiB (two slack rows)
+    static constexpr int VLOADS = 10;             // 32 x 20 slots = 10 KiB
+    static constexpr int KTILE = KLOADS * 1024;
+    static constexpr int VTILE = VLOADS * 1024;
+    static constexpr int KLW = (KLOADS + 3) / 4;
+    static constexpr int VLW = (VLOADS + 3) / 4;
+};
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
+    using C = DqCfg;
+    constexpr int BM = 128;
     __shared__ __attribute__((aligned(1024))) uint8_t kr0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::VTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t vr0[C::KTILE];
@@ -197,8 +214,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardParams p) {
     const int b = bk / p.Hkv, hkv = bk % p.Hkv, hq = hkv * p.group + g;
     const PrefillParams m = mask_params(p);
 
-    const int r0 = qt * C::BM;
-    const int r_last = min(r0 + C::BM, p.Nq) - 1;
+    const int r0 = qt * BM;
+    const int r_last = min(r0 + BM, p.Nq) - 1;
     const int w0 = r0 + wave * 32;
     const int w_last = min(w0 + 31, p.Nq - 1);
     const int row = w0 + (lane & 31);
@@ -215,7 +232,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardParams p) {
     bf16x8 qf[kBD / 16], df[kBD / 16];
     load_fragment(p.q + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, qf);
     load_fragment(p.dO + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, df);
-    // rows past Nq get weight 0 (their -LSE is -inf) and D = 0
     const float nl = row_ok ? p.ws_nl[head_row + row] : -__builtin_inff();
     const float Drow = row_ok ? p.ws_d[head_row + row] : 0.f;
 
@@ -246,21 +262,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BackwardParams p) {
         const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < p.sink_end);
         if (!active) return;
         const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < p.sink_end);
-        f32x16 s[2], dp[2];
-        rows_times(kr + kbase, qf, s);    // S^T = K Q^T
-        rows_times(vr + kbase, df, dp);   // dP^T = V dO^T
+        // S^T = K Q^T and dP^T = V dO^T, one 32-key block each
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const uint8_t* krl = kr + kbase;
+        const uint8_t* vrl = vr + kbase;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int kk = 0; kk < kBD / 16; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *(const u32x4*)(krl + kk * 32)), qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *(const u32x4*)(vrl + kk * 32)), df[kk], dp, 0, 0, 0);
+        }
+        order_operand_reads<kBD / 8, 1, 4>();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = n0 + jb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl));
-                if (!full && (key > hi_i || (key < lo_i && key >= p.sink_end))) pr = 0.f;
-                s[jb][r] = pr * (dp[jb][r] - Drow);   // dS^T
+        for (int r = 0; r < 16; ++r) {
+            const int key = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, nl));
+            if (!full && (key > hi_i || (key < lo_i && key >= p.sink_end))) pr = 0.f;
+            s[r] = pr * (dp[r] - Drow);   // dS^T
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kb * 8 + 2 * e], s[kb * 8 + 2 * e + 1]);
+            dsf[kb] = __builtin_bit_cast(bf16x8, w);
+        }
+        // dQ^T += K^T dS^T
+        const uint8_t* ktl = kt + vbase;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cb = 0; cb < kBD / 32; ++cb) {
+                const uint8_t* vp = ktl + kb * 16 * C::VS * 16 + cb * 64;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), dsf[kb], acc[cb], 0, 0, 0);
             }
-        bf16x8 dsf[4];
-        pack_operands(s, dsf);
-        tr_times(kt + vbase, dsf, acc);   // dQ^T += K^T dS^T
+        order_operand_reads<kBD / 16, 2, 2>();
     };
 
     if (tr.n > 0) {
