@@ -40,7 +40,7 @@ __device__ __forceinline__ bf16x8 row_operand(const uint8_t* rl, int jb, int kk)
 // A operand of a 32x32x16 MFMA read transposed from a transpose-padded tile
 // (two ds_read_b64_tr_b16): column cb*32 + (lane & 31) of tile rows
 // kb*16 + 8 (t / 4) + 4 (lane >> 5) + t % 4, t = 0..7, the row order of the
-// B operand built from a 32x32 accumulator (see pack_operands).  tl = this
+// B operand packed from a 32x32 accumulator's registers in order.  tl = this
 // lane's base, tile + vbase.
 __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tl, int kb, int cb) {
     using C = PrefillBf16Cfg<kBD>;
@@ -77,31 +77,6 @@ __device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)
         for (int jb = 0; jb < 2; ++jb)
             acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(rl, jb, kk), bf[kk], acc[jb], 0, 0, 0);
     order_operand_reads<kBD / 8, 1, 4>();
-}
-
-// acc[cb] += sum_kb A(transposed tile) x pf[kb]: a (d x 64) by (64 x 32)
-// product accumulated into a 128 x 32 accumulator (16 MFMAs).
-__device__ __forceinline__ void tr_times(const uint8_t* tl, const bf16x8 (&pf)[4], f32x16 (&acc)[kBD / 32]) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int cb = 0; cb < kBD / 32; ++cb)
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(tl, kb, cb), pf[kb], acc[cb], 0, 0, 0);
-    order_operand_reads<kBD / 8, 2, 2>();
-}
-
-// A 64 x 32 accumulator pair as the bf16 B operand of the next product, one
-// per 16-row block (the register order of a 32x32 accumulator is the
-// permuted row order tr_operand reads).
-__device__ __forceinline__ void pack_operands(const f32x16 (&x)[2], bf16x8 (&pf)[4]) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int jb = kb >> 1, h = (kb & 1) * 8;
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[jb][h + 2 * e], x[jb][h + 2 * e + 1]);
-        pf[kb] = __builtin_bit_cast(bf16x8, w);
-    }
 }
 
 // Store a d x 32 accumulator (column = this lane's row or key) as one bf16
@@ -441,42 +416,83 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
         rows_times(dr + kbase, vf, dp);   // dP = dO V^T
         const float* nl = (const float*)st;
         const float* dd = (const float*)(st + BQ * 4);
-        const int32_t* rlo = (const int32_t*)(st + 2 * BQ * 4);
-        const int32_t* rhi = (const int32_t*)(st + 3 * BQ * 4);
+        if (!full) {
+            // scores of invisible (row, key) pairs and of rows past Nq become
+            // -inf, so their P and dS are 0 below
+            const int32_t* rlo = (const int32_t*)(st + 2 * BQ * 4);
+            const int32_t* rhi = (const int32_t*)(st + 3 * BQ * 4);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+            for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int rb = jb * 32 + 8 * g4 + 4 * (lane >> 5);   // first of this lane's 4 consecutive rows
-                const f32x4 nl4 = *(const f32x4*)(nl + rb);
-                const f32x4 dd4 = *(const f32x4*)(dd + rb);
-                int32_t lo4[4] = {0, 0, 0, 0}, hi4[4] = {0, 0, 0, 0};
-                if (!full) {
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int rb = jb * 32 + 8 * g4 + 4 * (lane >> 5);   // first of this lane's 4 consecutive rows
                     const u32x4 a = *(const u32x4*)(rlo + rb);
                     const u32x4 z = *(const u32x4*)(rhi + rb);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo4[e] = (int32_t)a[e];
-                        hi4[e] = (int32_t)z[e];
+                        const bool vis = q0 + rb + e < p.Nq && key <= (int32_t)z[e] &&
+                                         (key >= (int32_t)a[e] || key < p.sink_end);
+                        if (!vis) s[jb][4 * g4 + e] = -__builtin_inff();
                     }
                 }
+        }
+        // the rows' statistics for the whole tile
+        f32x4 nl4[8], dd4[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g4 + e;
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[e]));
-                    if (!full) {
-                        const bool vis = q0 + rb + e < p.Nq && key <= hi4[e] && (key >= lo4[e] || key < p.sink_end);
-                        if (!vis) pr = 0.f;
-                    }
-                    dp[jb][r] = pr * (dp[jb][r] - dd4[e]);   // dS
-                    s[jb][r] = pr;                            // P
-                }
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int rb = (q >> 2) * 32 + 8 * (q & 3) + 4 * (lane >> 5);
+            nl4[q] = *(const f32x4*)(nl + rb);
+            dd4[q] = *(const f32x4*)(dd + rb);
+        }
+        // P and dS of element e of 16-row block kb (scores s[jb][8 (kb & 1) + e])
+        auto element = [&](int kb, int e) __attribute__((always_inline)) {
+            const int jb = kb >> 1, r = 8 * (kb & 1) + e, q = 4 * jb + (r >> 2);
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[q][r & 3]));
+            dp[jb][r] = pr * (dp[jb][r] - dd4[q][r & 3]);   // dS
+            s[jb][r] = pr;                                  // P
+        };
         bf16x8 pf[4], dsf[4];
-        pack_operands(s, pf);
-        pack_operands(dp, dsf);
-        tr_times(dt + vbase, pf, dv);    // dV^T += dO^T P
-        tr_times(qt + vbase, dsf, dk);   // dK^T += Q^T dS
+        auto pack = [&](int kb) __attribute__((always_inline)) {
+            const int jb = kb >> 1, h = (kb & 1) * 8;
+            u32x4 wp, wd;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                wp[x] = pack_bf16x2(s[jb][h + 2 * x], s[jb][h + 2 * x + 1]);
+                wd[x] = pack_bf16x2(dp[jb][h + 2 * x], dp[jb][h + 2 * x + 1]);
+            }
+            pf[kb] = __builtin_bit_cast(bf16x8, wp);
+            dsf[kb] = __builtin_bit_cast(bf16x8, wd);
+        };
+        // product i: block kb = i / 8, head-dim block cb = (i / 2) % 4, dV (i even) or dK (i odd)
+        auto operand = [&](int i) __attribute__((always_inline)) {
+            return tr_operand(((i & 1) ? qt : dt) + vbase, i >> 3, (i >> 1) & 3);
+        };
+        // Block 0's P and dS first; then the 32 dV / dK products, each followed
+        // by one element of the next block's P and dS and the operand reads of
+        // the product two ahead, pinned in that order by scheduling barriers.
+        // At one wave per SIMD nothing else fills the matrix core while the
+        // exponentials issue; with all of them ahead of the products (the
+        // compiler's own order, also under group-barrier hints) the backward
+        // of C2 took 428 us, pinned 360 us.
+#pragma unroll
+        for (int x = 0; x < 8; ++x) element(0, x);
+        pack(0);
+        bf16x8 opr[3];
+        opr[0] = operand(0);
+        opr[1] = operand(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int kb = i >> 3, cb = (i >> 1) & 3;
+            if (i + 2 < 32) opr[(i + 2) % 3] = operand(i + 2);
+            if (i & 1) dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[i % 3], dsf[kb], dk[cb], 0, 0, 0);
+            else dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[i % 3], pf[kb], dv[cb], 0, 0, 0);
+            if (kb < 3) {
+                element(kb + 1, i & 7);
+                if ((i & 7) == 7) pack(kb + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     if (n_iter > 0) {
