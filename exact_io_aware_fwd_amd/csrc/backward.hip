@@ -413,7 +413,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
                           (lo_z <= k0w || k0w + 31 < p.sink_end);
         f32x16 s[2], dp[2];
         rows_times(qr + kbase, kf, s);    // S = Q K^T   (columns: this lane's key)
-        rows_times(dr + kbase, vf, dp);   // dP = dO V^T
         const float* nl = (const float*)st;
         const float* dd = (const float*)(st + BQ * 4);
         if (!full) {
@@ -444,12 +443,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
             nl4[q] = *(const f32x4*)(nl + rb);
             dd4[q] = *(const f32x4*)(dd + rb);
         }
-        // P and dS of element e of 16-row block kb (scores s[jb][8 (kb & 1) + e])
+        // dP = dO V^T, each product followed by two of the tile's 32 P = exp2(.)
+        {
+            dp[0] = f32x16{};
+            dp[1] = f32x16{};
+            const uint8_t* drl = dr + kbase;
+            bf16x8 ra[5];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = row_operand(drl, j & 1, j >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i + 4 < 16) ra[(i + 4) % 5] = row_operand(drl, (i + 4) & 1, (i + 4) >> 1);
+                dp[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % 5], vf[i >> 1], dp[i & 1], 0, 0, 0);
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int el = 2 * i + x, jb = el >> 4, r = el & 15, q = 4 * jb + (r >> 2);
+                    s[jb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[q][r & 3]));   // P
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // dS of element e of 16-row block kb (P already in s[jb][8 (kb & 1) + e])
         auto element = [&](int kb, int e) __attribute__((always_inline)) {
             const int jb = kb >> 1, r = 8 * (kb & 1) + e, q = 4 * jb + (r >> 2);
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[q][r & 3]));
-            dp[jb][r] = pr * (dp[jb][r] - dd4[q][r & 3]);   // dS
-            s[jb][r] = pr;                                  // P
+            dp[jb][r] = s[jb][r] * (dp[jb][r] - dd4[q][r & 3]);   // dS
         };
         bf16x8 pf[4], dsf[4];
         auto pack = [&](int kb) __attribute__((always_inline)) {
@@ -467,13 +485,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
         auto operand = [&](int i) __attribute__((always_inline)) {
             return tr_operand(((i & 1) ? qt : dt) + vbase, i >> 3, (i >> 1) & 3);
         };
-        // Block 0's P and dS first; then the 32 dV / dK products, each followed
-        // by one element of the next block's P and dS and the operand reads of
-        // the product two ahead, pinned in that order by scheduling barriers.
-        // At one wave per SIMD nothing else fills the matrix core while the
-        // exponentials issue; with all of them ahead of the products (the
+        // Block 0's dS first; then the 32 dV / dK products, each followed by
+        // one element of the next block's dS and the operand reads of the
+        // product two ahead, pinned in that order by scheduling barriers.  At
+        // one wave per SIMD nothing else fills the matrix core while VALU work
+        // issues: with the exponentials and dS all ahead of the products (the
         // compiler's own order, also under group-barrier hints) the backward
-        // of C2 took 428 us, pinned 360 us.
+        // of C2 took 428 us; pinned under the products, 360 us; with the
+        // exponentials moved under the dP products as well, 345 us.
 #pragma unroll
         for (int x = 0; x < 8; ++x) element(0, x);
         pack(0);
