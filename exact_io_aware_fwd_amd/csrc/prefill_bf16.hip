@@ -90,11 +90,52 @@ __device__ __forceinline__ float bit_select(uint32_t mask, float a, float b) {
     return out;
 }
 
-// S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
-// key tile resident in LDS.  kl / vl point at this lane's own base in the
-// K / V tile; every other operand address is a compile-time offset from it.
+// Where a lane's MFMA operands sit in a K / V tile in LDS.
+//
+// PaddedTiles: rows padded to KS / VS 16-byte slots.  k / v point at this
+// lane's own base; every other operand address is a compile-time offset.
 template <int D>
-__device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t* kl, const uint8_t* vl, int n0,
+struct PaddedTiles {
+    using C = PrefillBf16Cfg<D>;
+    const uint8_t* k;
+    const uint8_t* v;
+    // K operand: rows (lane & 31) + 32 jb, 16-byte chunk 2 kk + (lane >> 5)
+    __device__ __forceinline__ const uint8_t* k_at(int jb, int kk) const { return k + jb * 32 * C::KS * 16 + kk * 32; }
+    // V^T operand (two transposing reads, the second 8 rows below the first)
+    __device__ __forceinline__ const uint8_t* v_at(int kb, int cb) const { return v + kb * 16 * C::VS * 16 + cb * 64; }
+    static constexpr int kVHalf = 8 * C::VS * 16;
+};
+
+// SwizzledTiles (d = 128): unpadded 256-byte rows, 16-byte chunk c of row r
+// stored at chunk c ^ (r % 16) in K tiles and c ^ 4 (r % 4) in V tiles.  A
+// 1 KiB direct copy then covers 4 whole rows (one page of a paged cache per
+// copy), and both operand reads stay free of bank conflicts: the 16 lanes of
+// a K row read hit 16 different chunks, and the 4 rows x 4 chunks of a
+// transposing V read land in 16 different chunks.  The lane-dependent part of
+// each address is a per-lane table (8 K and 4 V offsets).
+struct SwizzledTiles {
+    const uint8_t* k;
+    const uint8_t* v;
+    int ko[8];
+    int vo[4];
+    __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            ko[kk] = (lane & 31) * 256 + (((2 * kk + (lane >> 5)) ^ (lane & 15)) * 16);
+        const int t = (lane >> 2) & 3, i = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            vo[cb] = (4 * (lane >> 5) + t) * 256 + (4 * (cb ^ t) + i) * 16 + 8 * (lane & 1);
+    }
+    __device__ __forceinline__ const uint8_t* k_at(int jb, int kk) const { return k + jb * 32 * 256 + ko[kk]; }
+    __device__ __forceinline__ const uint8_t* v_at(int kb, int cb) const { return v + kb * 16 * 256 + vo[cb]; }
+    static constexpr int kVHalf = 8 * 256;
+};
+
+// S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
+// key tile resident in LDS, laid out as T says.
+template <int D, class T>
+__device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, int n0,
                                           bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane) {
     using C = PrefillBf16Cfg<D>;
     // ---- S^T = K Q^T, two 32-key blocks
@@ -105,7 +146,7 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
     for (int kk = 0; kk < C::DK; ++kk)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const u32x4 a = *(const u32x4*)(kl + jb * 32 * C::KS * 16 + kk * 32);
+            const u32x4 a = *(const u32x4*)tl.k_at(jb, kk);
             s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), st.qf[kk], s[jb], 0, 0, 0);
         }
     order_reads_ahead<2 * C::DK, 1, 4>();
@@ -189,9 +230,9 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const uint8_t
         const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
-            const uint8_t* vp = vl + kb * 16 * C::VS * 16 + cb * 64;
+            const uint8_t* vp = tl.v_at(kb, cb);
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + T::kVHalf));
             const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
             st.acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf, st.acc[cb], 0, 0, 0);
@@ -303,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
             const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
             if (active) {
                 const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-                tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
+                tile_step<D>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
             }
         };
 
@@ -344,11 +385,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
 // Chunked prefill over the paged KV cache.  The tile compute is tile_step
 // above; what changes is where rows come from.  Query rows are the chunk's
 // tokens (token-major), and a 64-key K/V tile is four 16-token pages that
-// the block table scatters over the page pool, so the copies gather rows
-// with per-lane 64-bit addresses (global_load_lds_dwordx4: lane l's 16 bytes
-// still land at LDS base + 16 l).  Rows at or past the sequence's end read
-// this all-zero row instead, so a page tail's contents (any bit pattern,
-// NaN included) never reach P V: its keys are masked and its values are 0.
+// the block table scatters over the page pool.  Rows at or past the
+// sequence's end must read as zeros, so a page tail's contents (any bit
+// pattern, NaN included) never reach P V: their keys are masked and their
+// values are 0.  Head dim 128 uses page-aligned tiles (paged_prefill_swz_kernel
+// below).  Head dim 64 keeps the padded tiles: the copies gather rows with
+// per-lane 64-bit addresses (global_load_lds_dwordx4: lane l's 16 bytes still
+// land at LDS base + 16 l), and rows past the end read this all-zero row.
 __device__ __attribute__((aligned(16))) uint16_t kZeroRow[128];
 
 // (row, chunk) of the padded tile layout that each of this wave's direct
@@ -498,7 +541,170 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
         const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
         if (active) {
             const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-            tile_step<D>(st, kc + kbase, vc + vbase, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
+            tile_step<D>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
+        }
+    };
+
+    if (tr.n > 0) {
+        const int t0 = tile_of(tr, 0);
+        copy_tile(t0, entries(t0), k_lds0, v_lds0);
+        if (tr.n > 1) next = entries(tile_of(tr, 1));
+        for (int it = 0; it < tr.n; it += 2) {
+            stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
+    }
+    const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    if (row_ok) {
+        const float s2 = pp.sink_logits != nullptr ? pp.sink_logits[hq] * kLog2e : neg_inf();
+        float inv, lse_row;
+        finish_row(st.m_run, l_tot, lf_tot, s2, inv, lse_row);
+        uint16_t* orow = pp.o + (size_t)(q0 + row) * row_stride + (size_t)hq * D;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 w;
+                w[0] = pack_bf16x2(st.acc[cb][4 * gq + 0] * inv, st.acc[cb][4 * gq + 1] * inv);
+                w[1] = pack_bf16x2(st.acc[cb][4 * gq + 2] * inv, st.acc[cb][4 * gq + 3] * inv);
+                *(u32x2*)(orow + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
+            }
+        if (pp.lse != nullptr && lane < 32)
+            pp.lse[(size_t)(q0 + row) * pp.Hq + hq] = lse_row;
+    }
+}
+
+// Chunked prefill at d = 128 with page-aligned tiles (SwizzledTiles): each
+// 1 KiB copy reads 4 rows of one page through a buffer resource made for that
+// page, whose range ends at the sequence's last key, so rows past it read as
+// zero in hardware and a lane's source offset is the same for every tile.
+// (The padded layout's copies cross page boundaries and needed per-lane
+// 64-bit page selects and zero-row selects: about 170 VALU instructions per
+// tile and wave.)
+template <bool SINKS>
+__global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillParams pp) {
+    constexpr int D = 128;
+    using C = PrefillBf16Cfg<D>;
+    constexpr int TILE = C::BN * D * 2;   // 16 KiB
+    const int sink_end = SINKS ? pp.sink_end : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bk, qt, g;
+    decode_work_pair_major(blockIdx.x, pp.num_seqs * pp.Hkv, pp.num_q_tiles, pp.group, bk, qt, g);
+    const int seq = bk / pp.Hkv, hkv = bk % pp.Hkv, hq = hkv * pp.group + g;
+    // per-sequence values, made wave-uniform so everything built from them
+    // (tile ranges, the per-page buffer resources) stays in scalar registers
+    const int q0 = __builtin_amdgcn_readfirstlane(pp.q_offsets[seq]);
+    const int nq = __builtin_amdgcn_readfirstlane(pp.q_offsets[seq + 1]) - q0;   // chunk length
+    const int L = __builtin_amdgcn_readfirstlane(pp.seq_lens[seq]);              // cached keys, the chunk included
+    const int r0 = qt * C::BM;
+    if (r0 >= nq) return;                        // whole workgroup: this chunk is shorter
+
+    PrefillParams p;
+    p.Nq = nq;
+    p.Nk = L;
+    p.mask_kind = pp.mask_kind;
+    p.window = pp.window;
+    p.doc_offsets = nullptr;
+    p.num_docs = 0;
+    p.sink_end = sink_end;
+    p.q_tile_pairs = 0;
+
+    const int r_last = min(r0 + C::BM, nq) - 1;
+    const int w0 = r0 + wave * 32;
+    const int w_last = min(w0 + 31, nq - 1);
+    const int row = w0 + (lane & 31);
+    const bool row_ok = row < nq;
+
+    int lo_i, hi_i;
+    row_interval(p, row, lo_i, hi_i);
+    int lo_wg, tmp, hi_wg;
+    row_interval(p, r0, lo_wg, tmp);
+    row_interval(p, r_last, tmp, hi_wg);
+    int lo_w_first, hi_w_first, lo_w_last, hi_w_last;
+    row_interval(p, w0, lo_w_first, hi_w_first);
+    row_interval(p, w_last, lo_w_last, hi_w_last);
+    const bool wave_has_rows = w0 < nq;
+
+    const size_t row_stride = (size_t)pp.Hq * D;   // token-major rows
+    PrefillBf16State<D> st;
+    {
+        const uint16_t* qrow = pp.q + (size_t)(q0 + (row_ok ? row : 0)) * row_stride + (size_t)hq * D;
+#pragma unroll
+        for (int kk = 0; kk < C::DK; ++kk) {
+            u32x4 w = row_ok ? *(const u32x4*)(qrow + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+            st.qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
+    st.m_run = neg_inf();
+    st.l_run = 0.f;
+    st.l_f32 = 0.f;
+
+    const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
+
+    // Copy jj (0..3) of this wave fills tile rows 16 jj + 4 wave .. + 3, i.e.
+    // rows 4 wave .. + 3 of the tile's page jj; lane l brings physical chunk
+    // l % 16 of row 4 wave + l / 16, which holds the swizzled logical chunk.
+    const int rip = 4 * wave + (lane >> 4);
+    const uint32_t kvo = (uint32_t)(rip * 256 + (((lane & 15) ^ rip) * 16));
+    const uint32_t vvo = (uint32_t)(rip * 256 + (((lane & 15) ^ (4 * ((lane >> 4) & 3))) * 16));
+    SwizzledTiles tl;
+    tl.init(lane);
+
+    const int32_t* bt = pp.block_table + (size_t)seq * pp.max_pages;
+    const int last_page = max((L + 15) / 16 - 1, 0);
+    const size_t head_off = (size_t)hkv * 16 * D;
+    const size_t page_elems = (size_t)pp.Hkv * 16 * D;
+    struct Pages { int32_t e0, e1, e2, e3; };
+    auto entries = [&](int t) __attribute__((always_inline)) {
+        const int lp = t * (C::BN / 16);
+        Pages pg;
+        pg.e0 = bt[min(lp + 0, last_page)];
+        pg.e1 = bt[min(lp + 1, last_page)];
+        pg.e2 = bt[min(lp + 2, last_page)];
+        pg.e3 = bt[min(lp + 3, last_page)];
+        return pg;
+    };
+    auto copy_tile = [&](int t, const Pages& pg, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int32_t e[4] = {__builtin_amdgcn_readfirstlane(pg.e0), __builtin_amdgcn_readfirstlane(pg.e1),
+                              __builtin_amdgcn_readfirstlane(pg.e2), __builtin_amdgcn_readfirstlane(pg.e3)};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            // rows of this page that exist (uniform, so the resource stays scalar)
+            const int valid = __builtin_amdgcn_readfirstlane(min(max(L - (t * C::BN + 16 * jj), 0), 16));
+            const size_t off = (size_t)e[jj] * page_elems + head_off;
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(pp.k_pages + off), (short)0, valid * D * 2, 0x00020000);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(pp.v_pages + off), (short)0, valid * D * 2, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + (4 * jj + wave) * 1024), 16, kvo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + (4 * jj + wave) * 1024), 16, vvo, 0, 0, 0);
+        }
+#endif
+    };
+
+    Pages next;
+    auto stage = [&](int it, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of this tile landed
+        __syncthreads();
+        if (it + 1 < tr.n) {
+            copy_tile(tile_of(tr, it + 1), next, kn, vn);
+            if (it + 2 < tr.n) next = entries(tile_of(tr, it + 2));
+        }
+        const int n0 = tile_of(tr, it) * C::BN;
+        const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
+        if (active) {
+            const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
+            tl.k = kc;
+            tl.v = vc;
+            tile_step<D>(st, tl, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
         }
     };
 
@@ -536,8 +742,8 @@ int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t st
     const int blocks = p.num_seqs * p.Hq * p.num_q_tiles;
     const bool sinks = p.sink_end > 0;
     if (d == 128) {
-        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, p);
+        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<true>), dim3(blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<false>), dim3(blocks), dim3(256), 0, stream, p);
     } else {
         if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
         else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
