@@ -57,7 +57,7 @@ KERNEL_WORKLOADS = {
     "prefill_bf16_kernel<128, false>": PREFILL_CONFIG,
     "decode_split_kernel<128>": DECODE_CONFIG,
     "decode_combine_kernel<128>": DECODE_CONFIG,
-    "paged_prefill_bf16_kernel<128, false>": CHUNKED_CONFIG,
+    "paged_prefill_swz_kernel<false>": CHUNKED_CONFIG,
     "bwd_prep_kernel": "backward of " + PREFILL_CONFIG,
     "bwd_dq_kernel": "backward of " + PREFILL_CONFIG,
     "bwd_dkdv_kernel": "backward of " + PREFILL_CONFIG,
@@ -408,7 +408,7 @@ def time_chunked(K: int, W: int) -> dict:
             "us": round(us, 2), "flop_per_call": flops,
             "workload": f"{CHUNKED_CONFIG} ({c['num_seqs']} seqs, Hq{c['Hq']} Hkv{c['Hkv']} d{c['d']}, "
                         f"{int(c['q_offsets'][-1])} chunk tokens over {int(c['seq_lens'].sum())} cached, causal)",
-            "kernel": f"paged_prefill_bf16_kernel<{c['d']}, false>"}
+            "kernel": "paged_prefill_swz_kernel<false>" if c["d"] == 128 else f"paged_prefill_bf16_kernel<{c['d']}, false>"}
 
 
 # ------------------------------------------------------- counter summaries
@@ -497,7 +497,7 @@ def summarize_clock(d: str) -> int:
             if row.get("Counter_Name") == "GRBM_GUI_ACTIVE":
                 cyc[row["Dispatch_Id"]] = cyc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
     flops = {"prefill_bf16_kernel<128, false>": prefill_flops(workloads.prefill_config(PREFILL_CONFIG)),
-             "paged_prefill_bf16_kernel<128, false>": chunked_flops(workloads.chunked_config(CHUNKED_CONFIG))}
+             "paged_prefill_swz_kernel<false>": chunked_flops(workloads.chunked_config(CHUNKED_CONFIG))}
     out = {"source_sha256": source_digest(),
            "command": "rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE -f csv -d <dir> -o run -- "
                       "python3 bench.py --pmc-pass ; python3 bench.py --summarize-clock <dir>",
