@@ -29,7 +29,12 @@ Readings of points the pages leave open (kept identical in the kernels):
     when a learned per-head sink is given);
   * sink tokens keep the first keys visible beside a sliding window, and a
     learned per-head sink logit joins each row's softmax denominator with a
-    zero value (AIB, Sliding windows and local:global layers).
+    zero value (AIB, Sliding windows and local:global layers);
+  * score modifications (FlexAttention's score_mod, "Attention and matrix
+    kernels" page, How it works) act on the scaled score of a visible pair
+    before the mask: a soft cap c turns it into c·tanh(score / c), then an
+    ALiBi-style per-head slope m adds m·(j - pos) with pos = i + Nk - Nq the
+    query's key position; the sink logit is not modified.
 
 Parity pins: see tests/test_oracle_pins.py (brute force in 50-digit
 arithmetic, closed forms, invariants, reductions and the worked example the
@@ -94,8 +99,8 @@ def visibility(Nq: int, Nk: int, mask: str, window: int = 0, doc_offsets=None,
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: str = "none",
               window: int = 0, doc_offsets=None, rows=None, row_block: int = 1024,
-              sink_tokens: int = 0, sink_logits=None):
-    """O = softmax(scale·Q·Kᵀ + mask)·V and LSE, in float64.
+              sink_tokens: int = 0, sink_logits=None, softcap: float = 0.0, alibi_slopes=None):
+    """O = softmax(mod(scale·Q·Kᵀ) + mask)·V and LSE, in float64.
 
     q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d] (float64).  Returns o with q's
     shape (or [B, Hq, len(rows), d] when ``rows`` selects query rows) and
@@ -108,6 +113,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
     head's sink and whose value is zero.  It only enlarges the denominator:
     O = Σ e^s v / (Σ e^s + e^sink), LSE = ln(Σ e^s + e^sink); a row with no
     visible key gets O = 0 and LSE = sink.  ``sink_tokens``: see visibility.
+
+    ``softcap`` > 0 and ``alibi_slopes`` [Hq] (optional) are the score
+    modifications: score -> softcap·tanh(score / softcap), then
+    score + slope[h]·(j - pos_i), pos_i = i + Nk - Nq.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -122,6 +131,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
     row_idx = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_idx.size
     sinks = None if sink_logits is None else np.asarray(sink_logits, dtype=np.float64).reshape(Hq)
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64).reshape(Hq)
+    softcap = float(softcap)
+    if softcap < 0 or not np.isfinite(softcap):
+        raise ValueError("softcap must be finite and >= 0")
     o = np.zeros((B, Hq, R, d), dtype=np.float64)
     lse = np.full((B, Hq, R), -np.inf, dtype=np.float64)
     if sinks is not None:
@@ -136,8 +149,12 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, mask: s
         for b in range(B):
             for h in range(Hq):
                 hk = h // group
-                # step 1: scores for the full rows, then the additive mask
+                # step 1: scores for the full rows, their modifications, then the additive mask
                 s = scale * (q[b, h, sel, :] @ k[b, hk].T)
+                if softcap > 0:
+                    s = softcap * np.tanh(s / softcap)
+                if slopes is not None:         # key position minus the query's key position
+                    s = s + slopes[h] * (np.arange(Nk)[None, :] - (sel + Nk - Nq)[:, None])
                 s = np.where(vis, s, -np.inf)
                 if sinks is not None:          # the sink joins each row as one more score
                     s = np.concatenate([s, np.full((sel.size, 1), sinks[h])], axis=1)
@@ -207,7 +224,8 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
 
 def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
                   seq_lens: np.ndarray, q_offsets: np.ndarray, scale: float, mask: str = "causal",
-                  window: int = 0, seqs=None, dtype: str = "f64", sink_tokens: int = 0, sink_logits=None):
+                  window: int = 0, seqs=None, dtype: str = "f64", sink_tokens: int = 0, sink_logits=None,
+                  softcap: float = 0.0, alibi_slopes=None):
     """Chunked prefill over a paged KV cache, in float64.
 
     The serving pattern that pairs a tiled attention kernel with KV paging
@@ -247,7 +265,7 @@ def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block
                 ks, vs = ks.astype(np.float64), vs.astype(np.float64)
             qs = np.transpose(q[a:b], (1, 0, 2))[None]          # [1, Hq, n, d]
             os_, ls_ = attention(qs, ks[None], vs[None], scale, mask, window, sink_tokens=sink_tokens,
-                                 sink_logits=sink_logits)
+                                 sink_logits=sink_logits, softcap=softcap, alibi_slopes=alibi_slopes)
             o = np.transpose(os_[0], (1, 0, 2))
             lse = np.transpose(ls_[0], (1, 0))
         outs_o.append(o)

@@ -1,0 +1,190 @@
+"""Pins of the oracle's score modifications (soft cap, ALiBi-style slopes).
+
+The modifications act on each visible pair's scaled score before the mask
+(FlexAttention's score_mod, "Attention and matrix kernels" page, How it
+works): score -> c·tanh(score / c), then + m_h·(j - pos_i) with
+pos_i = i + Nk - Nq.  Each test fixes them by something other than the
+oracle's own formula:
+
+  * closed forms: two keys whose scores are c·atanh(a) cap to exactly c·a,
+    and zero queries make the ALiBi weights a geometric series;
+  * limits: a cap far above the scores leaves plain attention, a cap far
+    below them leaves uniform weights over the visible keys;
+  * a bound: capped logits lie in [-c, c], so |LSE - ln n_visible| <= c;
+  * a reduction: the ALiBi bias is one more head-dim coordinate (m_h / scale
+    on the query, the key index on the key), with the query's own constant
+    -m_h·pos_i moved into the LSE;
+  * brute force in 50-digit arithmetic on tiny inputs, both modifications on,
+    for every mask kind.
+"""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _two_keys(c, a, scale):
+    """q [1,1,1,2], k [1,1,2,2] whose scaled scores are c·atanh(a_j)."""
+    x = c * np.arctanh(np.asarray(a, dtype=np.float64))
+    q = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    k = np.stack([x / scale, np.zeros(2)], axis=1).reshape(1, 1, 2, 2)
+    return q, k
+
+
+def test_softcap_two_keys_closed_form():
+    c, scale = 3.0, 0.7
+    a = [0.5, -0.25]
+    q, k = _two_keys(c, a, scale)
+    v = np.array([[2.0, -1.0], [5.0, 3.0]]).reshape(1, 1, 2, 2)
+    o, lse = oracle.attention(q, k, v, scale, softcap=c)
+    w = np.exp(c * np.array(a))                   # capped scores are exactly c·a_j
+    np.testing.assert_allclose(lse[0, 0, 0], math.log(w.sum()), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o[0, 0, 0], (w[:, None] * v[0, 0]).sum(0) / w.sum(), rtol=0, atol=1e-13)
+
+
+def test_softcap_then_alibi_closed_form():
+    # the cap acts first, the bias is added to the capped score: with Nq = 1,
+    # Nk = 2 the query sits at position 1, so key j gets m·(j - 1)
+    c, scale, m = 2.0, 1.3, 0.75
+    a = [0.9, -0.6]
+    q, k = _two_keys(c, a, scale)
+    v = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 1, 2, 2)
+    o, lse = oracle.attention(q, k, v, scale, "causal", softcap=c, alibi_slopes=[m])
+    z = c * np.array(a) + m * (np.arange(2) - 1)
+    w = np.exp(z)
+    np.testing.assert_allclose(lse[0, 0, 0], math.log(w.sum()), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o[0, 0, 0], w / w.sum(), rtol=0, atol=1e-13)
+
+
+def test_softcap_limits_and_bound():
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 9, 13, 8
+    q, k, v = 3 * rnd(1, B, Hq, Nq, d), 3 * rnd(2, B, Hkv, Nk, d), rnd(3, B, Hkv, Nk, d)
+    for mask, window in (("none", 0), ("causal", 0), ("window", 4)):
+        plain = oracle.attention(q, k, v, 0.6, mask, window)
+        big = oracle.attention(q, k, v, 0.6, mask, window, softcap=1e7)
+        np.testing.assert_allclose(big[0], plain[0], rtol=0, atol=1e-9)
+        np.testing.assert_allclose(big[1], plain[1], rtol=0, atol=1e-9)
+        # c -> 0: every capped logit -> 0, uniform weights over the visible keys
+        vis = oracle.visibility(Nq, Nk, mask, window)
+        n = vis.sum(1)
+        small = oracle.attention(q, k, v, 0.6, mask, window, softcap=1e-9)
+        for h in range(Hq):
+            mean = (vis.astype(float) @ v[0, h // 2]) / np.maximum(n, 1)[:, None]
+            np.testing.assert_allclose(small[0][0, h], mean, rtol=0, atol=1e-8)
+            np.testing.assert_allclose(small[1][0, h], np.where(n > 0, np.log(np.maximum(n, 1)), -np.inf),
+                                       rtol=0, atol=1e-8)
+        # any cap: |LSE - ln n| <= c
+        for cap in (0.5, 2.0, 7.0):
+            l = oracle.attention(q, k, v, 0.6, mask, window, softcap=cap)[1][0]
+            assert np.all(np.abs(l - np.log(n)[None, :]) <= cap + 1e-12)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, 0.6, softcap=-1.0)
+
+
+def test_alibi_geometric_closed_form():
+    # q = 0: scores are all zero, so row i's weights are e^{m (j - pos_i)}
+    # over its visible keys j = 0..pos_i (causal): a geometric series
+    Nq, Nk, d, m = 5, 8, 4, 0.4
+    q = np.zeros((1, 1, Nq, d))
+    k, v = rnd(11, 1, 1, Nk, d), rnd(12, 1, 1, Nk, d)
+    o, lse = oracle.attention(q, k, v, 0.5, "causal", alibi_slopes=[m])
+    r = math.exp(m)
+    for i in range(Nq):
+        pos = i + Nk - Nq
+        tot = (r ** (pos + 1) - 1) / (r - 1) * math.exp(-m * pos)   # sum_{j<=pos} e^{m (j - pos)}
+        np.testing.assert_allclose(lse[0, 0, i], math.log(tot), rtol=0, atol=1e-12)
+        w = np.array([r ** j for j in range(pos + 1)])
+        np.testing.assert_allclose(o[0, 0, i], (w[:, None] * v[0, 0, :pos + 1]).sum(0) / w.sum(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 3)])
+def test_alibi_is_one_more_coordinate(mask, window):
+    B, Hq, Hkv, Nq, Nk, d, scale = 2, 4, 2, 6, 11, 5, 0.45
+    q, k, v = rnd(21, B, Hq, Nq, d), rnd(22, B, Hkv, Nk, d), rnd(23, B, Hkv, Nk, d)
+    slopes = np.array([0.5, 0.125, -0.3, 0.0])
+    o, lse = oracle.attention(q, k, v, scale, mask, window, alibi_slopes=slopes)
+    qe = np.concatenate([q, np.broadcast_to((slopes / scale)[None, :, None, None], (B, Hq, Nq, 1))], axis=3)
+    ke = np.concatenate([k, np.broadcast_to(np.arange(Nk, dtype=float)[None, None, :, None], (B, Hkv, Nk, 1))], axis=3)
+    ve = np.concatenate([v, np.zeros((B, Hkv, Nk, 1))], axis=3)
+    oe, le = oracle.attention(qe, ke, ve, scale, mask, window)
+    pos = np.arange(Nq) + Nk - Nq
+    np.testing.assert_allclose(o, oe[..., :d], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, le - slopes[None, :, None] * pos[None, None, :], rtol=0, atol=1e-11)
+
+
+def _brute_mods(q, k, v, scale, mask, window, offsets, cap, slopes):
+    mpmath.mp.dps = 50
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros(q.shape)
+    L = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Nq):
+                pos = i + Nk - Nq
+                if mask == "none":
+                    keys = range(Nk)
+                elif mask == "causal":
+                    keys = [j for j in range(Nk) if j <= pos]
+                elif mask == "window":
+                    keys = [j for j in range(Nk) if pos - window < j <= pos]
+                else:
+                    start = max([a for a in offsets[:-1] if a <= pos], default=None) if pos >= 0 else None
+                    keys = [] if start is None else [j for j in range(Nk) if start <= j <= pos]
+                z = {}
+                for j in keys:
+                    x = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, h, i, c]) * mpmath.mpf(k[b, h // g, j, c])
+                                                        for c in range(d))
+                    x = mpmath.mpf(cap) * mpmath.tanh(x / cap)
+                    z[j] = x + mpmath.mpf(slopes[h]) * (j - pos)
+                if not z:
+                    continue
+                w = {j: mpmath.exp(z[j]) for j in z}
+                tot = mpmath.fsum(w.values())
+                for c in range(d):
+                    O[b, h, i, c] = float(mpmath.fsum(w[j] * mpmath.mpf(v[b, h // g, j, c]) for j in z) / tot)
+                L[b, h, i] = float(mpmath.log(tot))
+    return O, L
+
+
+@pytest.mark.parametrize("mask,window,offsets", [
+    ("none", 0, None), ("causal", 0, None), ("window", 2, None), ("document", 0, [0, 3, 4, 8]),
+])
+def test_score_mods_brute_force_tiny(mask, window, offsets):
+    B, Hq, Hkv, d, Nq, Nk = 1, 4, 2, 3, 6, 8
+    q, k, v = 2 * rnd(31, B, Hq, Nq, d), 2 * rnd(32, B, Hkv, Nk, d), rnd(33, B, Hkv, Nk, d)
+    slopes = np.array([0.25, -0.5, 1.0, 0.0625])
+    o, lse = oracle.attention(q, k, v, 0.9, mask, window, doc_offsets=offsets, softcap=1.5, alibi_slopes=slopes)
+    ob, lb = _brute_mods(q, k, v, 0.9, mask, window, offsets, 1.5, slopes)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-13)
+
+
+def test_paged_prefill_carries_the_mods():
+    # a single chunk covering the whole cache is plain attention on the gathered sequence
+    c = workloads.make_chunked_prefill(2, 4, 2, 8, chunks=[5, 3], prefixes=[7, 0], seed=5, tail_fill="nan")
+    slopes = np.array([0.5, -0.25, 0.125, 1.0])
+    op, lp = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                  c["q_offsets"], c["scale"], "causal", dtype="bf16", softcap=2.0,
+                                  alibi_slopes=slopes)
+    plain = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                 c["q_offsets"], c["scale"], "causal", dtype="bf16")
+    assert not np.allclose(op, plain[0])
+    offs = c["q_offsets"]
+    for s in range(2):
+        L = int(c["seq_lens"][s])
+        k_seq = oracle.from_bf16_bits(oracle.gather_sequence(c["k_pages"], c["block_table"][s], L))
+        v_seq = oracle.from_bf16_bits(oracle.gather_sequence(c["v_pages"], c["block_table"][s], L))
+        qs = np.transpose(oracle.to_f64(c["q"], "bf16")[offs[s]:offs[s + 1]], (1, 0, 2))[None]
+        o, l = oracle.attention(qs, k_seq[None], v_seq[None], c["scale"], "causal", softcap=2.0, alibi_slopes=slopes)
+        np.testing.assert_array_equal(op[offs[s]:offs[s + 1]], np.transpose(o[0], (1, 0, 2)))
+        np.testing.assert_array_equal(lp[offs[s]:offs[s + 1]], np.transpose(l[0], (1, 0)))
