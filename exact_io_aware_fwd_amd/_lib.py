@@ -25,7 +25,8 @@ MASK_KINDS = {"none": 0, "causal": 1, "window": 2, "document": 3}
 class AttnMask(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("doc_offsets", ctypes.c_void_p), ("num_docs", ctypes.c_int32),
-                ("sink_tokens", ctypes.c_int32), ("sink_logits", ctypes.c_void_p)]
+                ("sink_tokens", ctypes.c_int32), ("sink_logits", ctypes.c_void_p),
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
 
 
 _lib = None

@@ -39,13 +39,21 @@ def _sink_ptr(sink_logits: torch.Tensor | None, Hq: int):
 
 
 def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
-              sink_tokens: int = 0, sink_logits: torch.Tensor | None = None, Hq: int = 0) -> _lib.AttnMask:
+              sink_tokens: int = 0, sink_logits: torch.Tensor | None = None, Hq: int = 0,
+              softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None) -> _lib.AttnMask:
     _need(mask in _lib.MASK_KINDS, f"unknown mask {mask!r}")
     m = _lib.AttnMask()
     m.kind = _lib.MASK_KINDS[mask]
     m.window = int(window) if mask == "window" else 0
     m.sink_tokens = int(sink_tokens)
     m.sink_logits = _sink_ptr(sink_logits, Hq)
+    m.softcap = float(softcap)
+    if alibi_slopes is not None:
+        _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and alibi_slopes.is_contiguous()
+              and alibi_slopes.numel() == Hq, "alibi_slopes must be a contiguous float32 device tensor of Hq entries")
+        m.alibi_slopes = alibi_slopes.data_ptr()
+    else:
+        m.alibi_slopes = None
     if mask == "document":
         _need(doc_offsets is not None and doc_offsets.dtype == torch.int32 and doc_offsets.is_cuda
               and doc_offsets.is_contiguous(), "document mask needs int32 device doc_offsets")
@@ -60,10 +68,12 @@ def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | N
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float | None = None,
              mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
              sink_tokens: int = 0, sink_logits: torch.Tensor | None = None,
+             softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None, with_lse: bool = True,
              stream=None):
     """Attention forward: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> (o [B,Hq,Nq,d], lse [B,Hq,Nq] fp32).
-    sink_tokens (window mask) and sink_logits [Hq] fp32 are the optional attention sinks."""
+    sink_tokens (window mask) and sink_logits [Hq] fp32 are the optional attention sinks;
+    softcap and alibi_slopes [Hq] fp32 the optional score modifications (bf16 only)."""
     _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-d [B, H, N, d]")
     _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "dtype must be bf16 or fp32, same for q/k/v")
     _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous device tensors")
@@ -76,7 +86,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq)
+    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                              None if lse is None else ctypes_ptr(lse),
                              B, Hq, Hkv, Nq, Nk, d, float(scale), m, _DTYPES[q.dtype], _stream(stream))
@@ -127,6 +137,7 @@ def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
                        block_table: torch.Tensor, seq_lens: torch.Tensor, q_offsets: torch.Tensor, *,
                        max_seq_len: int, max_q_len: int, scale: float | None = None, mask: str = "causal",
                        window: int = 0, sink_tokens: int = 0, sink_logits: torch.Tensor | None = None,
+                       softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                        with_lse: bool = True, stream=None):
     """Chunked prefill over the paged cache: q [T,Hq,d] token-major, pages [P,Hkv,16,d],
@@ -148,7 +159,7 @@ def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    m = make_mask(mask, window, None, sink_tokens, sink_logits, Hq)
+    m = make_mask(mask, window, None, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_paged_prefill(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
                                        ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(q_offsets),
                                        ctypes_ptr(out), None if lse is None else ctypes_ptr(lse),
@@ -165,7 +176,8 @@ def attn_bwd_workspace_size(B: int, Hq: int, Nq: int) -> int:
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
              lse: torch.Tensor, *, scale: float | None = None, mask: str = "none", window: int = 0,
              doc_offsets: torch.Tensor | None = None, sink_tokens: int = 0,
-             sink_logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+             sink_logits: torch.Tensor | None = None, softcap: float = 0.0,
+             alibi_slopes: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """Attention backward from the forward's o and lse: -> (dq, dk, dv, dsink); dsink is None
     without sink_logits.  bf16, d = 128; dk/dv sum over each KV head's query heads."""
     _need(all(t.dim() == 4 for t in (q, k, v, o, do)), "q, k, v, o, do must be 4-d")
@@ -182,7 +194,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     need = attn_bwd_workspace_size(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq)
+    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o), ctypes_ptr(do),
                              ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk), ctypes_ptr(dv),
                              None if dsink is None else ctypes_ptr(dsink), B, Hq, Hkv, Nq, Nk, d, float(scale), m,

@@ -37,6 +37,14 @@ bool sinks_ok(const attn_mask& m) {
     return ((uintptr_t)m.sink_logits & 3u) == 0;
 }
 
+// score modifications: soft cap finite and >= 0 (NaN fails), slopes 4-byte aligned
+bool mods_ok(const attn_mask& m) {
+    if (!(m.softcap >= 0.f) || m.softcap == __builtin_inff()) return false;
+    return ((uintptr_t)m.alibi_slopes & 3u) == 0;
+}
+
+bool has_mods(const attn_mask& m) { return m.softcap > 0.f || m.alibi_slopes != nullptr; }
+
 }  // namespace
 
 extern "C" const char* attn_status_string(int status) {
@@ -59,10 +67,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_DOCUMENT && (mask.num_docs < 1 || mask.doc_offsets == nullptr))
         return ATTN_ERR_INVALID_ARGUMENT;
-    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (has_mods(mask) && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hq * Nq == 0) return ATTN_OK;  // nothing to write
     if (q == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
@@ -85,6 +94,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.q_tile_pairs = 0;
     p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
     p.sink_logits = mask.sink_logits;
+    p.softcap = mask.softcap;
+    p.alibi_slopes = mask.alibi_slopes;
 
     if (dtype == ATTN_DTYPE_BF16)
         xattn::launch_prefill_bf16(p, d, stream);
@@ -150,7 +161,7 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind < ATTN_MASK_NONE || mask.kind > ATTN_MASK_DOCUMENT) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
-    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_DOCUMENT) return ATTN_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
@@ -179,6 +190,8 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.window : 0;
     p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
     p.sink_logits = mask.sink_logits;
+    p.softcap = mask.softcap;
+    p.alibi_slopes = mask.alibi_slopes;
     xattn::launch_paged_prefill_bf16(p, d, stream);
     return hip_status(hipGetLastError());
 }
@@ -198,10 +211,10 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (mask.kind == ATTN_MASK_SLIDING_WINDOW && mask.window < 1) return ATTN_ERR_INVALID_ARGUMENT;
     if (mask.kind == ATTN_MASK_DOCUMENT && (mask.num_docs < 1 || mask.doc_offsets == nullptr))
         return ATTN_ERR_INVALID_ARGUMENT;
-    if (!sinks_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-    if (dtype != ATTN_DTYPE_BF16 || d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_DTYPE_BF16 || d != 128 || has_mods(mask)) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hkv * Nk == 0 && (long long)B * Hq * Nq == 0) return ATTN_OK;
     if (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr) {

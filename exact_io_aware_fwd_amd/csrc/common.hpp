@@ -39,6 +39,8 @@ struct PrefillParams {
     int q_tile_pairs;          // > 0: workgroup u takes query tiles num_q_tiles-1-u and u (set by the launcher)
     int sink_end;              // window mask: keys [0, sink_end) stay visible too (0: none)
     const float* sink_logits;  // [Hq] learned sink logit per query head, or null
+    float softcap;             // > 0: score -> softcap * tanh(score / softcap); 0: off
+    const float* alibi_slopes; // [Hq] or null: score += slope * (key - query position)
 };
 
 // Arguments of one chunked-prefill launch over the paged cache (validated on
@@ -60,9 +62,35 @@ struct PagedPrefillParams {
     int window;
     int sink_end;               // window mask: keys [0, sink_end) stay visible too
     const float* sink_logits;   // [Hq] or null
+    float softcap;              // as in PrefillParams
+    const float* alibi_slopes;
 };
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Score modifications of one query head, in the base-2 domain of the
+// kernels (FlexAttention's score_mod, "Attention and matrix kernels" page,
+// How it works).  With x = scale * q.k, a soft cap c gives
+//   c tanh(x / c) = c - 2c / (e^(2x/c) + 1),   e^(2x/c) = 2^(q.k * cap_k),
+// and the ALiBi-style bias adds slope * (key - query position) after it.
+// The logit times log2(e) is then cap_l2 - 2 cap_l2 / (2^(q.k cap_k) + 1) +
+// slope_l2 * (key - query position); without a cap the first terms are
+// q.k * scale_l2.
+struct ScoreMod {
+    float cap_k;      // 2 scale log2(e) / c; 0: no cap
+    float cap_l2;     // c log2(e)
+    float scale_l2;   // scale log2(e)
+    float slope_l2;   // this head's slope times log2(e); 0 without slopes
+};
+
+__device__ __forceinline__ ScoreMod make_score_mod(float scale_log2, float softcap, const float* slopes, int hq) {
+    ScoreMod m;
+    m.cap_k = softcap > 0.f ? 2.f * scale_log2 / softcap : 0.f;
+    m.cap_l2 = softcap * kLog2e;
+    m.scale_l2 = scale_log2;
+    m.slope_l2 = slopes != nullptr ? slopes[hq] * kLog2e : 0.f;
+    return m;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

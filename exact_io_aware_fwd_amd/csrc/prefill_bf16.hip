@@ -133,10 +133,12 @@ struct SwizzledTiles {
 };
 
 // S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
-// key tile resident in LDS, laid out as T says.
-template <int D, class T>
+// key tile resident in LDS, laid out as T says.  MODS: the scores first go
+// through the score modifications sm (qpos: this lane's query position).
+template <int D, bool MODS = false, class T>
 __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, int n0,
-                                          bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane) {
+                                          bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane,
+                                          const ScoreMod& sm = ScoreMod{}, int qpos = 0) {
     using C = PrefillBf16Cfg<D>;
     // ---- S^T = K Q^T, two 32-key blocks
     f32x16 s[2];
@@ -150,6 +152,31 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
             s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), st.qf[kk], s[jb], 0, 0, 0);
         }
     order_reads_ahead<2 * C::DK, 1, 4>();
+    // ---- score modifications: raw q.k -> base-2 logit (unit scale below).
+    // Score 16 jb + r of this lane is key n0 + 4 (lane / 32) + 32 jb +
+    // 8 (r / 4) + r % 4 (see the mask below).  They come before the mask, so
+    // a masked key still ends at -inf.
+    if constexpr (MODS) {
+        const float b0 = sm.slope_l2 * (float)(n0 + 4 * (lane >> 5) - qpos);
+        if (sm.cap_k != 0.f) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = fast_exp2(s[jb][r] * sm.cap_k);
+                    const float capped = __builtin_fmaf(-2.f * sm.cap_l2, __builtin_amdgcn_rcpf(e + 1.f), sm.cap_l2);
+                    s[jb][r] = capped + __builtin_fmaf(sm.slope_l2, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), b0);
+                }
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[jb][r] = __builtin_fmaf(s[jb][r], sm.scale_l2,
+                                              __builtin_fmaf(sm.slope_l2, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), b0));
+        }
+        scale_log2 = 1.f;
+    }
     // ---- mask, only where the tile is not fully visible to this wave
     if (!full) {
         // Score i = 16 jb + r of this lane is key base + c_i with the
@@ -245,8 +272,10 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
 
 // SINKS: the window mask keeps sink tokens visible (the second key interval);
 // without it the tile loop and the mask compile to the one-interval form.
-template <int D, bool SINKS>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
+// MODS: the score modifications are on (a kernel of its own, so the plain
+// kernel's code does not change).
+template <int D, bool SINKS, bool MODS>
+__device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
     using C = PrefillBf16Cfg<D>;
     const int sink_end = SINKS ? p.sink_end : 0;
     // two stages of the K/V ring, as separate arrays so each access names its buffer
@@ -261,6 +290,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
     int bk, unit, g;
     decode_work(blockIdx.x, nbk, p.q_tile_pairs > 0 ? p.q_tile_pairs : p.num_q_tiles, p.group, bk, unit, g);
     const int b = bk / p.Hkv, hkv = bk % p.Hkv, hq = hkv * p.group + g;
+    const ScoreMod sm = MODS ? make_score_mod(p.scale_log2, p.softcap, p.alibi_slopes, hq) : ScoreMod{};
 
     const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
     const uint16_t* __restrict__ kg_ = (const uint16_t*)p.k + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
@@ -344,7 +374,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
             const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
             if (active) {
                 const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-                tile_step<D>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane);
+                tile_step<D, MODS>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end,
+                                   p.scale_log2, lane, sm, row + p.Nk - p.Nq);
             }
         };
 
@@ -379,6 +410,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
             if (p.lse != nullptr && lane < 32) p.lse[((size_t)b * p.Hq + hq) * (size_t)p.Nq + row] = lse_row;
         }
     }
+}
+
+template <int D, bool SINKS>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
+    prefill_bf16_body<D, SINKS, false>(p);
+}
+
+template <int D, bool SINKS>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_mod_kernel(PrefillParams p) {
+    prefill_bf16_body<D, SINKS, true>(p);
 }
 
 // ------------------------------------------------------------------------
@@ -427,8 +468,8 @@ __device__ __forceinline__ void load_paged_tile_async(const uint16_t* __restrict
     }
 }
 
-template <int D, bool SINKS>
-__global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefillParams pp) {
+template <int D, bool SINKS, bool MODS>
+__device__ __forceinline__ void paged_prefill_bf16_body(PagedPrefillParams pp) {
     using C = PrefillBf16Cfg<D>;
     const int sink_end = SINKS ? pp.sink_end : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
@@ -441,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     int bk, qt, g;
     decode_work_pair_major(blockIdx.x, pp.num_seqs * pp.Hkv, pp.num_q_tiles, pp.group, bk, qt, g);
     const int seq = bk / pp.Hkv, hkv = bk % pp.Hkv, hq = hkv * pp.group + g;
+    const ScoreMod sm = MODS ? make_score_mod(pp.scale_log2, pp.softcap, pp.alibi_slopes, hq) : ScoreMod{};
     const int q0 = pp.q_offsets[seq];
     const int nq = pp.q_offsets[seq + 1] - q0;   // chunk length
     const int L = pp.seq_lens[seq];              // cached keys, the chunk included
@@ -541,7 +583,8 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
         const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
         if (active) {
             const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-            tile_step<D>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
+            tile_step<D, MODS>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end,
+                               pp.scale_log2, lane, sm, row + L - nq);
         }
     };
 
@@ -575,6 +618,16 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
     }
 }
 
+template <int D, bool SINKS>
+__global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefillParams pp) {
+    paged_prefill_bf16_body<D, SINKS, false>(pp);
+}
+
+template <int D, bool SINKS>
+__global__ __launch_bounds__(256, 2) void paged_prefill_bf16_mod_kernel(PagedPrefillParams pp) {
+    paged_prefill_bf16_body<D, SINKS, true>(pp);
+}
+
 // Chunked prefill at d = 128 with page-aligned tiles (SwizzledTiles): each
 // 1 KiB copy reads 4 rows of one page through a buffer resource made for that
 // page, whose range ends at the sequence's last key, so rows past it read as
@@ -582,8 +635,8 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(PagedPrefill
 // (The padded layout's copies cross page boundaries and needed per-lane
 // 64-bit page selects and zero-row selects: about 170 VALU instructions per
 // tile and wave.)
-template <bool SINKS>
-__global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillParams pp) {
+template <bool SINKS, bool MODS>
+__device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
     constexpr int D = 128;
     using C = PrefillBf16Cfg<D>;
     constexpr int TILE = C::BN * D * 2;   // 16 KiB
@@ -598,6 +651,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillP
     int bk, qt, g;
     decode_work_pair_major(blockIdx.x, pp.num_seqs * pp.Hkv, pp.num_q_tiles, pp.group, bk, qt, g);
     const int seq = bk / pp.Hkv, hkv = bk % pp.Hkv, hq = hkv * pp.group + g;
+    const ScoreMod sm = MODS ? make_score_mod(pp.scale_log2, pp.softcap, pp.alibi_slopes, hq) : ScoreMod{};
     // per-sequence values, made wave-uniform so everything built from them
     // (tile ranges, the per-page buffer resources) stays in scalar registers
     const int q0 = __builtin_amdgcn_readfirstlane(pp.q_offsets[seq]);
@@ -704,7 +758,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillP
             const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
             tl.k = kc;
             tl.v = vc;
-            tile_step<D>(st, tl, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane);
+            tile_step<D, MODS>(st, tl, n0, full, lo_i, hi_i, sink_end, pp.scale_log2, lane, sm, row + L - nq);
         }
     };
 
@@ -738,15 +792,37 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillP
     }
 }
 
+template <bool SINKS>
+__global__ __launch_bounds__(256, 2) void paged_prefill_swz_kernel(PagedPrefillParams pp) {
+    paged_prefill_swz_body<SINKS, false>(pp);
+}
+
+template <bool SINKS>
+__global__ __launch_bounds__(256, 2) void paged_prefill_swz_mod_kernel(PagedPrefillParams pp) {
+    paged_prefill_swz_body<SINKS, true>(pp);
+}
+
 int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t stream) {
     const int blocks = p.num_seqs * p.Hq * p.num_q_tiles;
     const bool sinks = p.sink_end > 0;
+    const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
+    const dim3 g(blocks), wg(256);
     if (d == 128) {
-        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<true>), dim3(blocks), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<false>), dim3(blocks), dim3(256), 0, stream, p);
+        if (mods) {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_mod_kernel<true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_mod_kernel<false>), g, wg, 0, stream, p);
+        } else {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_swz_kernel<false>), g, wg, 0, stream, p);
+        }
     } else {
-        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
+        if (mods) {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_mod_kernel<64, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_mod_kernel<64, false>), g, wg, 0, stream, p);
+        } else {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(paged_prefill_bf16_kernel<64, false>), g, wg, 0, stream, p);
+        }
     }
     return 0;
 }
@@ -778,12 +854,24 @@ int launch_prefill_bf16(const PrefillParams& p0, int d, hipStream_t stream) {
     p.q_tile_pairs = pair ? (p.num_q_tiles + 1) / 2 : 0;
     const int blocks = p.B * p.Hq * (p.q_tile_pairs > 0 ? p.q_tile_pairs : p.num_q_tiles);
     const bool sinks = p.sink_end > 0;
+    const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
+    const dim3 g(blocks), wg(256);
     if (d == 128) {
-        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, p);
+        if (mods) {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<128, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<128, false>), g, wg, 0, stream, p);
+        } else {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<128, false>), g, wg, 0, stream, p);
+        }
     } else {
-        if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
+        if (mods) {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<64, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<64, false>), g, wg, 0, stream, p);
+        } else {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, true>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_kernel<64, false>), g, wg, 0, stream, p);
+        }
     }
     return 0;
 }

@@ -79,6 +79,20 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  *                   value: O = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink}),
  *                   LSE = ln(sum_j e^{s_j} + e^{sink}); a row that sees no key
  *                   gets O = 0 and LSE = sink.
+ *
+ * Score modifications ("Attention and matrix kernels", How it works: the
+ * FlexAttention entry names score modifications as one family of variants;
+ * the page names none in particular, and these two are the menu this library
+ * offers).  Both act on s = scale * q.k before the mask, in this order:
+ *   softcap         > 0: s becomes softcap * tanh(s / softcap), which bounds
+ *                   every score by softcap.  0: off.  Finite, >= 0.
+ *   alibi_slopes    NULL, or a DEVICE float32 array of Hq entries, 4-byte
+ *                   aligned: s gets slope[h] * (j - pos) added, a linear
+ *                   penalty on the distance from the query's position pos to
+ *                   key j (pos = i + Nk - Nq, as for the causal mask).
+ * Supported by attn_fwd with bf16 and by attn_paged_prefill; attn_fwd with
+ * f32 and attn_bwd return ATTN_ERR_UNSUPPORTED when either is set.  Sink
+ * logits are not modified.
  */
 typedef enum {
     ATTN_MASK_NONE = 0,
@@ -94,6 +108,8 @@ typedef struct {
     int32_t num_docs;           /* DOCUMENT only: >= 1 */
     int32_t sink_tokens;        /* SLIDING_WINDOW only: sink tokens kept visible, >= 0 */
     const float* sink_logits;   /* NULL or device [Hq]: learned sink logit per query head */
+    float softcap;              /* > 0: scores become softcap * tanh(score / softcap); 0: off */
+    const float* alibi_slopes;  /* NULL or device [Hq]: score += slope * (key - query position) */
 } attn_mask;
 
 /*

@@ -10,6 +10,11 @@ import oracle
 
 BF16_TOL = dict(max_abs=1e-2, mean_abs=1e-3, lse=1e-3)
 F32_TOL = dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-3)
+# Sharp attention (ALiBi slopes, large scales) gives outputs of a few units,
+# where bf16 itself is coarse: the output's rounding costs up to 2^-9 |o| and
+# the bf16 softmax weights of the P V product another 2^-9 relative, so the
+# bound grows by 2^-8 |o_ref| on top of the absolute 1e-2.
+BF16_SHARP_TOL = dict(max_abs=1e-2, mean_abs=1e-3, lse=1e-3, rel=2.0 ** -8)
 
 
 def say(*a):
@@ -45,12 +50,18 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
         assert np.all(np.isneginf(lse_gpu[empty])), f"{label}: fully masked rows must have LSE -inf"
     assert np.all(np.isfinite(lse_gpu[~empty])), f"{label}: non-finite LSE on a visible row"
     err = np.abs(o_gpu - o_ref)
+    # max-abs is checked on err - rel |o_ref| (rel 0: plain max-abs); mean-abs on err itself
+    bound_err = err - tol.get("rel", 0.0) * np.abs(o_ref)
     lerr = np.abs(lse_gpu[~empty] - lse_ref[~empty]) if (~empty).any() else np.zeros(1)
     summary = dict(max_abs=float(err.max()) if err.size else 0.0, mean_abs=float(err.mean()) if err.size else 0.0,
                    lse_max_abs=float(lerr.max()))
     say(f"[parity] {label}: {summary}")
     assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite output"
-    assert summary["max_abs"] <= tol["max_abs"], f"{label}: max-abs {summary['max_abs']} > {tol['max_abs']}"
+    if tol.get("rel", 0.0) > 0.0:
+        worst = float(bound_err.max()) if err.size else 0.0
+        assert worst <= tol["max_abs"], f"{label}: max of |err| - {tol['rel']} |o| is {worst} > {tol['max_abs']}"
+    else:
+        assert summary["max_abs"] <= tol["max_abs"], f"{label}: max-abs {summary['max_abs']} > {tol['max_abs']}"
     assert summary["mean_abs"] <= tol["mean_abs"], f"{label}: mean-abs {summary['mean_abs']} > {tol['mean_abs']}"
     assert summary["lse_max_abs"] <= tol["lse"], f"{label}: LSE max-abs {summary['lse_max_abs']} > {tol['lse']}"
     return summary

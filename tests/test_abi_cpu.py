@@ -39,8 +39,8 @@ def test_status_strings():
 
 
 def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.1,
-        kind=0, window=0, doc=None, num_docs=0, dtype=1, sink_tokens=0, sinks=None):
-    m = _lib.AttnMask(kind, window, doc, num_docs, sink_tokens, sinks)
+        kind=0, window=0, doc=None, num_docs=0, dtype=1, sink_tokens=0, sinks=None, softcap=0.0, alibi=None):
+    m = _lib.AttnMask(kind, window, doc, num_docs, sink_tokens, sinks, softcap, alibi)
     return _lib.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype, None)
 
 
@@ -54,6 +54,9 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16
     (dict(Nq=1 << 29), 2),
     (dict(kind=1, sink_tokens=4), 1), (dict(kind=0, sink_tokens=1), 1), (dict(kind=2, window=8, sink_tokens=-1), 1),
     (dict(sinks=FAKE + 2), 1), (dict(kind=2, window=8, sink_tokens=4, d=96), 2),
+    (dict(softcap=-1.0), 1), (dict(softcap=float("nan")), 1), (dict(softcap=float("inf")), 1),
+    (dict(alibi=FAKE + 2), 1), (dict(softcap=5.0, dtype=0), 2), (dict(alibi=FAKE, dtype=0), 2),
+    (dict(softcap=5.0, d=96), 2),
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
@@ -99,8 +102,9 @@ def test_workspace_size():
 
 
 def chunked(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qo=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128,
-            page=16, max_pages=4, max_len=64, max_q=32, scale=0.1, kind=1, window=0, sink_tokens=0, sinks=None):
-    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks)
+            page=16, max_pages=4, max_len=64, max_q=32, scale=0.1, kind=1, window=0, sink_tokens=0, sinks=None,
+            softcap=0.0, alibi=None):
+    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks, softcap, alibi)
     return _lib.lib().attn_paged_prefill(q, kp, vp, bt, sl, qo, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
                                          max_q, scale, m, None)
 
@@ -112,6 +116,7 @@ def chunked(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qo=FAKE, o=FAKE, lse=FAK
     (dict(sl=None), 1), (dict(bt=None), 1), (dict(kp=FAKE + 2), 1), (dict(o=FAKE + 8), 1),
     (dict(max_len=1 << 29, max_pages=1 << 25), 2),
     (dict(kind=1, sink_tokens=2), 1), (dict(sinks=FAKE + 2), 1),
+    (dict(softcap=-2.0), 1), (dict(softcap=float("nan")), 1), (dict(alibi=FAKE + 1), 1),
 ])
 def test_paged_prefill_rejects_bad_arguments(kw, status):
     assert chunked(**kw) == status
@@ -123,10 +128,11 @@ def test_paged_prefill_empty_problems_are_noops():
 
 
 def bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dsink=None, B=1, Hq=4, Hkv=2,
-        Nq=16, Nk=16, d=128, scale=0.1, kind=1, window=0, dtype=1, ws=FAKE, ws_bytes=None, sink_tokens=0, sinks=None):
+        Nq=16, Nk=16, d=128, scale=0.1, kind=1, window=0, dtype=1, ws=FAKE, ws_bytes=None, sink_tokens=0, sinks=None,
+        softcap=0.0, alibi=None):
     if ws_bytes is None:
         ws_bytes = xa.attn_bwd_workspace_size(B, Hq, Nq)
-    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks)
+    m = _lib.AttnMask(kind, window, None, 0, sink_tokens, sinks, softcap, alibi)
     return _lib.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, dsink, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype,
                                ws, ws_bytes, None)
 
@@ -136,6 +142,7 @@ def bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=
     (dict(scale=0.0), 1), (dict(kind=9), 1), (dict(kind=2, window=0), 1), (dict(kind=1, sink_tokens=3), 1),
     (dict(q=None), 1), (dict(do=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(dq=FAKE + 8), 1),
     (dict(lse=FAKE + 2), 1), (dict(ws_bytes=8), 3), (dict(ws=None), 3), (dict(Nk=1 << 29), 2),
+    (dict(softcap=5.0), 2), (dict(alibi=FAKE), 2), (dict(softcap=-5.0), 1),
 ])
 def test_bwd_rejects_bad_arguments(kw, status):
     assert bwd(**kw) == status
