@@ -277,7 +277,7 @@ def paged_prefill(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
                        mask: str = "none", window: int = 0, doc_offsets=None, sink_tokens: int = 0,
-                       sink_logits=None):
+                       sink_logits=None, softcap: float = 0.0, alibi_slopes=None):
     """Gradients of attention, in float64: (dq, dk, dv, dsink).
 
     The backward pass the "Attention Is the Bottleneck" page describes for
@@ -291,6 +291,11 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
       dsink[h] = -Σ_i P_sink,i D_i         (the sink's value is zero)
     q, do [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d].  dk and dv sum over the query
     heads of each KV head's group.  dsink is None without sink logits.
+
+    With the score modifications (see ``attention``) S is the modified score
+    and dS its gradient; the chain rule through the cap multiplies it by
+    d(c tanh(x / c)) / dx = 1 - tanh²(x / c) before dQ and dK (the slope
+    bias does not depend on Q or K).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -300,6 +305,10 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     Hkv, Nk = k.shape[1], k.shape[2]
     group = Hq // Hkv
     sinks = None if sink_logits is None else np.asarray(sink_logits, dtype=np.float64).reshape(Hq)
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64).reshape(Hq)
+    softcap = float(softcap)
+    if softcap < 0 or not np.isfinite(softcap):
+        raise ValueError("softcap must be finite and >= 0")
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -308,7 +317,15 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     for b in range(B):
         for h in range(Hq):
             hk = h // group
-            s = np.where(vis, scale * (q[b, h] @ k[b, hk].T), -np.inf)
+            x = scale * (q[b, h] @ k[b, hk].T)
+            dx = np.ones_like(x)                       # d(modified score) / dx
+            if softcap > 0:
+                th = np.tanh(x / softcap)
+                x = softcap * th
+                dx = 1.0 - th * th
+            if slopes is not None:
+                x = x + slopes[h] * (np.arange(Nk)[None, :] - (np.arange(Nq) + Nk - Nq)[:, None])
+            s = np.where(vis, x, -np.inf)
             cols = [s] if sinks is None else [s, np.full((Nq, 1), sinks[h])]
             full = np.concatenate(cols, axis=1)
             m = np.max(full, axis=1, keepdims=True)
@@ -320,7 +337,7 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
             o = p @ v[b, hk]
             dP = do[b, h] @ v[b, hk].T
             D = np.sum(do[b, h] * o, axis=1, keepdims=True)
-            dS = p * (dP - D)
+            dS = p * (dP - D) * dx
             dq[b, h] = scale * (dS @ k[b, hk])
             dk[b, hk] += scale * (dS.T @ q[b, h])
             dv[b, hk] += p.T @ do[b, h]

@@ -188,3 +188,57 @@ def test_paged_prefill_carries_the_mods():
         o, l = oracle.attention(qs, k_seq[None], v_seq[None], c["scale"], "causal", softcap=2.0, alibi_slopes=slopes)
         np.testing.assert_array_equal(op[offs[s]:offs[s + 1]], np.transpose(o[0], (1, 0, 2)))
         np.testing.assert_array_equal(lp[offs[s]:offs[s + 1]], np.transpose(l[0], (1, 0)))
+
+
+# ---------------------------------------------------------------- backward
+
+def _mod_loss(q, k, v, do, scale, mask, window, offsets, cap, slopes):
+    o, _ = oracle.attention(q, k, v, scale, mask, window, offsets, softcap=cap, alibi_slopes=slopes)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("mask,window,offsets,Nq,Nk,cap,with_slopes", [
+    ("none", 0, None, 5, 6, 1.2, False), ("causal", 0, None, 6, 6, 0.0, True), ("causal", 0, None, 4, 7, 0.8, True),
+    ("window", 2, None, 6, 6, 2.0, True), ("document", 0, [0, 2, 5, 6], 6, 6, 1.5, True),
+])
+def test_mod_backward_matches_central_differences(mask, window, offsets, Nq, Nk, cap, with_slopes):
+    B, Hq, Hkv, d = 1, 4, 2, 3
+    q, k, v = 2 * rnd(131, B, Hq, Nq, d), 2 * rnd(132, B, Hkv, Nk, d), rnd(133, B, Hkv, Nk, d)
+    do = rnd(134, B, Hq, Nq, d)
+    slopes = np.array([0.3, -0.2, 0.7, 0.05]) if with_slopes else None
+    scale = 0.9
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, mask, window, offsets, softcap=cap,
+                                              alibi_slopes=slopes)
+    h = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _mod_loss(q, k, v, do, scale, mask, window, offsets, cap, slopes)
+            arr[idx] = old - h
+            lm = _mod_loss(q, k, v, do, scale, mask, window, offsets, cap, slopes)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=1e-7, err_msg=name)
+
+
+def test_mod_backward_matches_torch_autograd():
+    # an independent forward in torch (tanh cap, then the bias, then the
+    # causal mask), differentiated by autograd in float64
+    import torch
+    B, Hq, Hkv, Nq, Nk, d, scale, cap = 2, 4, 2, 30, 40, 16, 0.6, 2.5
+    q, k, v, do = 2 * rnd(141, B, Hq, Nq, d), 2 * rnd(142, B, Hkv, Nk, d), rnd(143, B, Hkv, Nk, d), rnd(144, B, Hq, Nq, d)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    pos = torch.arange(Nq)[:, None] + (Nk - Nq)
+    j = torch.arange(Nk)[None, :]
+    kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+    s = cap * torch.tanh(scale * tq @ kk.transpose(-1, -2) / cap)
+    s = s + torch.tensor(slopes)[None, :, None, None] * (j - pos).double()
+    s = s.masked_fill(~(j <= pos), float("-inf"))
+    (torch.softmax(s, dim=-1) @ vv * torch.tensor(do)).sum().backward()
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, "causal", softcap=cap, alibi_slopes=slopes)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12)
