@@ -214,7 +214,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-    if (dtype != ATTN_DTYPE_BF16 || d != 128 || has_mods(mask)) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_DTYPE_BF16 || d != 128) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hkv * Nk == 0 && (long long)B * Hq * Nq == 0) return ATTN_OK;
     if (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr) {
@@ -247,6 +247,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.num_docs = mask.kind == ATTN_MASK_DOCUMENT ? mask.num_docs : 0;
     p.sink_end = mask.kind == ATTN_MASK_SLIDING_WINDOW ? mask.sink_tokens : 0;
     p.sink_logits = mask.sink_logits;
+    p.softcap = mask.softcap;
+    p.alibi_slopes = mask.alibi_slopes;
     p.num_q_tiles = (int)q_tiles;
     p.num_k_tiles = (int)k_tiles;
     // with no query rows the dK/dV pass still runs and writes zeros

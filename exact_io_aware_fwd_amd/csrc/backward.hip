@@ -172,7 +172,13 @@ struct DqCfg {
     static constexpr int VLW = (VLOADS + 3) / 4;
 };
 
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
+// MODS: the scores went through the score modifications.  With t the
+// modified score and x = scale q.k, P = exp(t - LSE) and the gradient
+// P (dP - D) is with respect to t; the cap's chain-rule factor
+// dt/dx = 1 - tanh^2 = 4 r (1 - r), r = 1 / (e^(2x/c) + 1), turns it into
+// the gradient with respect to x (the slope bias does not depend on q or k).
+template <bool MODS>
+__device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     using C = DqCfg;
     constexpr int BM = 128;
     __shared__ __attribute__((aligned(1024))) uint8_t kr0[C::KTILE];
@@ -188,6 +194,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
     decode_work(blockIdx.x, p.B * p.Hkv, p.num_q_tiles, p.group, bk, qt, g);
     const int b = bk / p.Hkv, hkv = bk % p.Hkv, hq = hkv * p.group + g;
     const PrefillParams m = mask_params(p);
+    const ScoreMod sm = MODS ? make_score_mod(p.scale_log2, p.softcap, p.alibi_slopes, hq) : ScoreMod{};
 
     const int r0 = qt * BM;
     const int r_last = min(r0 + BM, p.Nq) - 1;
@@ -252,9 +259,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, nl));
+            float pr, fac = 1.f;
+            if constexpr (MODS) {
+                const float bias = sm.slope_l2 * (float)(key - (row + p.Nk - p.Nq));
+                float t;
+                if (sm.cap_k != 0.f) {
+                    const float rr = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s[r] * sm.cap_k) + 1.f);
+                    t = __builtin_fmaf(-2.f * sm.cap_l2, rr, sm.cap_l2) + bias;
+                    fac = 4.f * rr * (1.f - rr);
+                } else {
+                    t = __builtin_fmaf(s[r], sm.scale_l2, bias);
+                }
+                pr = __builtin_amdgcn_exp2f(t + nl);
+            } else {
+                pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, nl));
+            }
             if (!full && (key > hi_i || (key < lo_i && key >= p.sink_end))) pr = 0.f;
-            s[r] = pr * (dp[r] - Drow);   // dS^T
+            s[r] = MODS ? pr * (dp[r] - Drow) * fac : pr * (dp[r] - Drow);   // dS^T
         }
         bf16x8 dsf[2];
 #pragma unroll
@@ -290,9 +311,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
     if (row_ok) store_row(p.dq + (head_row + row) * kBD, acc, p.scale, lane);
 }
 
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) { bwd_dq_body<false>(p); }
+__global__ __launch_bounds__(256, 2) void bwd_dq_mod_kernel(BackwardParams p) { bwd_dq_body<true>(p); }
+
 // dK and dV: each wave owns 32 keys (K and V fragments in registers) and
 // streams 64-row query tiles of every query head of its group.
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
+// MODS: as for the dQ pass; each streamed tile's query head brings its own slope.
+template <bool MODS>
+__device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     using C = PrefillBf16Cfg<kBD>;
     constexpr int BQ = 64;    // query rows per streamed tile
     constexpr int BK = 128;   // keys per workgroup
@@ -413,6 +439,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
                           (lo_z <= k0w || k0w + 31 < p.sink_end);
         f32x16 s[2], dp[2];
         rows_times(qr + kbase, kf, s);    // S = Q K^T   (columns: this lane's key)
+        // MODS: S -> modified base-2 scores (before the mask: a capped -inf
+        // would come back finite) and the cap factor of each element.  Element
+        // (jb, r) is row q0 + 32 jb + 8 (r / 4) + 4 (lane / 32) + r % 4.
+        f32x16 fac[2];
+        if constexpr (MODS) {
+            const ScoreMod sm = make_score_mod(p.scale_log2, p.softcap, p.alibi_slopes, head_of(it));
+            const float b0 = sm.slope_l2 * (float)(key - q0 - 4 * (lane >> 5) - p.Nk + p.Nq);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float bias = __builtin_fmaf(-sm.slope_l2, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), b0);
+                    if (sm.cap_k != 0.f) {
+                        const float rr = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s[jb][r] * sm.cap_k) + 1.f);
+                        s[jb][r] = __builtin_fmaf(-2.f * sm.cap_l2, rr, sm.cap_l2) + bias;
+                        fac[jb][r] = 4.f * rr * (1.f - rr);
+                    } else {
+                        s[jb][r] = __builtin_fmaf(s[jb][r], sm.scale_l2, bias);
+                        fac[jb][r] = 1.f;
+                    }
+                }
+        }
+        const float sl = MODS ? 1.f : p.scale_log2;   // scores already in base-2 units under MODS
         const float* nl = (const float*)st;
         const float* dd = (const float*)(st + BQ * 4);
         if (!full) {
@@ -459,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int el = 2 * i + x, jb = el >> 4, r = el & 15, q = 4 * jb + (r >> 2);
-                    s[jb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], p.scale_log2, nl4[q][r & 3]));   // P
+                    s[jb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], sl, nl4[q][r & 3]));   // P
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -467,7 +516,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
         // dS of element e of 16-row block kb (P already in s[jb][8 (kb & 1) + e])
         auto element = [&](int kb, int e) __attribute__((always_inline)) {
             const int jb = kb >> 1, r = 8 * (kb & 1) + e, q = 4 * jb + (r >> 2);
-            dp[jb][r] = s[jb][r] * (dp[jb][r] - dd4[q][r & 3]);   // dS
+            if constexpr (MODS) dp[jb][r] = s[jb][r] * (dp[jb][r] - dd4[q][r & 3]) * fac[jb][r];   // dS
+            else dp[jb][r] = s[jb][r] * (dp[jb][r] - dd4[q][r & 3]);
         };
         bf16x8 pf[4], dsf[4];
         auto pack = [&](int kb) __attribute__((always_inline)) {
@@ -527,6 +577,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) {
     }
 }
 
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) { bwd_dkdv_body<false>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_mod_kernel(BackwardParams p) { bwd_dkdv_body<true>(p); }
+
 size_t backward_workspace_bytes(int B, int Hq, int Nq) {
     const size_t rows = (size_t)B * Hq * Nq;
     return 4 * ((rows * 4 + 255) / 256) * 256;
@@ -534,6 +587,7 @@ size_t backward_workspace_bytes(int B, int Hq, int Nq) {
 
 int launch_backward(BackwardParams p, void* ws, hipStream_t stream) {
     const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+    const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
     const size_t stride = ((rows * 4 + 255) / 256) * 256;
     p.ws_nl = (float*)ws;
     p.ws_d = (float*)((char*)ws + stride);
@@ -545,10 +599,13 @@ int launch_backward(BackwardParams p, void* ws, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_zero_kernel, dim3((p.Hq + 255) / 256), dim3(256), 0, stream, p.dsink, p.Hq);
     if (rows > 0) {
         hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
-        hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
+        if (mods) hipLaunchKernelGGL(bwd_dq_mod_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
     }
-    if ((long long)p.B * p.Hkv * p.num_k_tiles > 0)
-        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
+    if ((long long)p.B * p.Hkv * p.num_k_tiles > 0) {
+        if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
+    }
     return 0;
 }
 

@@ -31,6 +31,8 @@ struct BackwardParams {
     int num_docs;
     int sink_end;          // window mask: keys [0, sink_end) visible too
     const float* sink_logits;
+    float softcap;             // > 0: scores went through softcap * tanh(score / softcap)
+    const float* alibi_slopes; // [Hq] or null: score += slope * (key - query position)
     int num_q_tiles;       // 128-row query tiles (dQ pass)
     int num_k_tiles;       // 128-key tiles (dK/dV pass)
 };

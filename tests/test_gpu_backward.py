@@ -35,20 +35,23 @@ def check_grad(got, want, label):
     assert float(err.max()) <= REL_MAX * scale, f"{label}: max-abs {float(err.max())} > {REL_MAX} x {scale}"
 
 
-def run_case(c, label, sink_tokens=0, sinks=None):
+def run_case(c, label, sink_tokens=0, sinks=None, softcap=0.0, slopes=None):
     say(f"[case] {label} B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} Nq={c['Nq']} Nk={c['Nk']} mask={c['mask']} "
-        f"window={c['window']} sink_tokens={sink_tokens} sinks={'yes' if sinks is not None else 'no'}")
+        f"window={c['window']} sink_tokens={sink_tokens} sinks={'yes' if sinks is not None else 'no'} "
+        f"softcap={softcap} alibi={'yes' if slopes is not None else 'no'}")
     q, k, v, do = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16"), dev(c["do"], "bf16")
     sl = None if sinks is None else torch.from_numpy(sinks).cuda()
     kw = dict(scale=c["scale"], mask=c["mask"], window=c["window"], doc_offsets=doc_tensor(c),
-              sink_tokens=sink_tokens, sink_logits=sl)
+              sink_tokens=sink_tokens, sink_logits=sl, softcap=softcap,
+              alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda())
     o, lse = attn_fwd(q, k, v, **kw)
     dq, dk, dv, ds = attn_bwd(q, k, v, o, do, lse, **kw)
     torch.cuda.synchronize()
     ref = oracle.attention_backward(oracle.to_f64(c["q"], "bf16"), oracle.to_f64(c["k"], "bf16"),
                                     oracle.to_f64(c["v"], "bf16"), oracle.to_f64(c["do"], "bf16"), c["scale"],
                                     c["mask"], c["window"], c["doc_offsets"], sink_tokens,
-                                    None if sinks is None else sinks.astype(np.float64))
+                                    None if sinks is None else sinks.astype(np.float64), softcap=softcap,
+                                    alibi_slopes=None if slopes is None else slopes.astype(np.float64))
     for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
         check_grad(host_f64(got), want, f"{label} {name}")
     if sinks is not None:
@@ -82,3 +85,26 @@ def test_backward_sinks(sink_tokens, with_logits):
 def test_backward_larger_causal():
     c = workloads.make_backward(1, 8, 2, 2048, 2048, 128, seed=77, mask="causal")
     run_case(c, "bwd causal 2048 GQA")
+
+
+def alibi_slopes(Hq):
+    return np.array([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=np.float32)
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 100), ("document", 0)])
+@pytest.mark.parametrize("softcap,alibi", [(2.0, False), (0.0, True), (3.0, True)])
+def test_backward_score_mods(mask, window, softcap, alibi):
+    # scale 3/sqrt(d): scores of a few units, so the caps bend most of them
+    c = workloads.make_backward(1, 8, 2, 500, 500, 128, seed=77, mask=mask, window=window, doc_min=80,
+                                doc_max=300, scale=3.0 / np.sqrt(128))
+    run_case(c, f"bwd mods {mask} cap{softcap} alibi{alibi}", softcap=softcap,
+             slopes=alibi_slopes(8) if alibi else None)
+
+
+def test_backward_score_mods_ragged_with_sinks():
+    # Nq > Nk: the first rows see no key; window with sink tokens and learned sinks
+    c = workloads.make_backward(2, 4, 2, 300, 200, 128, seed=79, mask="causal", scale=0.2)
+    run_case(c, "bwd mods causal 300x200", softcap=1.5, slopes=alibi_slopes(4))
+    c = workloads.make_backward(1, 8, 2, 500, 500, 128, seed=81, mask="window", window=96, scale=0.2)
+    sinks = np.random.default_rng(82).normal(0.0, 2.0, 8).astype(np.float32)
+    run_case(c, "bwd mods window96 sinks", 4, sinks, softcap=2.5, slopes=alibi_slopes(8))
