@@ -43,8 +43,6 @@ bool mods_ok(const attn_mask& m) {
     return ((uintptr_t)m.alibi_slopes & 3u) == 0;
 }
 
-bool has_mods(const attn_mask& m) { return m.softcap > 0.f || m.alibi_slopes != nullptr; }
-
 }  // namespace
 
 extern "C" const char* attn_status_string(int status) {
@@ -71,7 +69,6 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-    if (has_mods(mask) && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hq * Nq == 0) return ATTN_OK;  // nothing to write
     if (q == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
@@ -86,6 +83,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
     p.group = Hq / Hkv;
     p.scale_log2 = scale * xattn::kLog2e;
+    p.scale = scale;
     p.mask_kind = mask.kind;
     p.window = mask.kind == ATTN_MASK_SLIDING_WINDOW ? (mask.window < Nk ? mask.window : (Nk > 0 ? Nk : 1)) : 0;
     p.doc_offsets = mask.kind == ATTN_MASK_DOCUMENT ? mask.doc_offsets : nullptr;

@@ -31,6 +31,7 @@ struct PrefillParams {
     int B, Hq, Hkv, Nq, Nk;
     int group;          // Hq / Hkv
     float scale_log2;   // scale * log2(e): scores go straight to the base-2 domain
+    float scale;        // scale itself (the fp32 kernel's score modifications)
     int mask_kind;
     int window;         // clamped to [1, Nk] on the host
     const int32_t* doc_offsets;

@@ -54,6 +54,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
     float m_run = neg_inf(), l_run = 0.f;
+    const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
+    const float slope_l2 = p.alibi_slopes != nullptr ? p.alibi_slopes[hq] * kLog2e : 0.f;
+    const int qpos = row + p.Nk - p.Nq;
+    const float sl = mods ? 1.f : p.scale_log2;   // scores in base-2 units after the modifications
 
     const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, BN);
     for (int it = 0; it < tr.n; ++it) {
@@ -76,6 +80,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
         for (int kk = 0; kk < DK; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_lds[(lane & 31) * KSTR + kk * 2 + (lane >> 5)], qf[kk], s, 0, 0, 0);
         const bool full = n0 + BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + BN - 1 < p.sink_end);
+        // score modifications (uniform branch): x = scale q.k, then the cap
+        // c tanh(x / c) and the bias slope (key - query position), into base-2
+        // units; the softmax below then runs at unit scale
+        if (mods) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float x = s[r] * p.scale;
+                if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
+                s[r] = __builtin_fmaf(x, kLog2e, slope_l2 * (float)(key - qpos));
+            }
+        }
         if (!full) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -87,13 +103,13 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt * p.scale_log2);
+        const float m_new = fmaxf(m_run, mt * sl);
         const float m_use = m_new == neg_inf() ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
+            const float e = fast_exp2(__builtin_fmaf(s[r], sl, -m_use));
             s[r] = e;
             psum += e;
         }

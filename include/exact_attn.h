@@ -90,10 +90,9 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  *                   aligned: s gets slope[h] * (j - pos) added, a linear
  *                   penalty on the distance from the query's position pos to
  *                   key j (pos = i + Nk - Nq, as for the causal mask).
- * Supported by attn_fwd with bf16, attn_paged_prefill and attn_bwd (which
- * differentiates through both: the cap contributes 1 - tanh^2 to dS); attn_fwd
- * with f32 returns ATTN_ERR_UNSUPPORTED when either is set.  Sink logits are
- * not modified.
+ * Supported by attn_fwd (both dtypes), attn_paged_prefill and attn_bwd (which
+ * differentiates through both: the cap contributes 1 - tanh^2 to dS).  Sink
+ * logits are not modified.
  */
 typedef enum {
     ATTN_MASK_NONE = 0,

@@ -1,7 +1,7 @@
 """Score modifications on the GPU against the fp64 oracle: a tanh soft cap
 and ALiBi-style per-head slopes, alone and together, over every mask kind,
-with sinks, in the bf16 prefill (d 128 and 64) and the chunked prefill; and
-the fp32 prefill, which rejects them (the backward's are in the backward tests)."""
+with sinks, in the bf16 prefill (d 128 and 64), the chunked prefill and the
+fp32 prefill (the backward's are in the backward tests)."""
 import math
 
 import numpy as np
@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import workloads
-from exact_io_aware_fwd_amd import AttnError, attn_fwd, attn_paged_prefill
-from _gpu_helpers import BF16_SHARP_TOL, compare, dev, doc_tensor, host_f64, say
+from exact_io_aware_fwd_amd import attn_fwd, attn_paged_prefill
+from _gpu_helpers import BF16_SHARP_TOL, F32_TOL, compare, dev, doc_tensor, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -98,10 +98,20 @@ def test_chunked_prefill_score_mods(d, mask, window):
     compare(host_f64(o), host_f64(lse), o_ref, l_ref, BF16_SHARP_TOL, f"chunked mods d{d} {mask}")
 
 
-def test_mods_rejected_by_fp32_prefill():
-    c = workloads.make_prefill(1, 4, 2, 64, 64, 128, dtype="f32", seed=99, mask="causal")
-    say("[case] score mods rejected by the fp32 prefill")
-    with pytest.raises(AttnError, match="unsupported"):
-        attn_fwd(dev(c["q"], "f32"), dev(c["k"], "f32"), dev(c["v"], "f32"), scale=c["scale"], mask="causal",
-                 softcap=5.0)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window,Nq,Nk", [("causal", 0, 256, 256), ("none", 0, 100, 170),
+                                               ("window", 40, 200, 230), ("document", 0, 256, 256)])
+def test_fp32_prefill_score_mods(d, mask, window, Nq, Nk):
+    # the fp32 path against the fp32 bound (max-abs 1e-5), soft cap and slopes together
+    c = workloads.make_prefill(1, 4, 2, Nq, Nk, d, dtype="f32", seed=99, mask=mask, window=window, doc_min=30,
+                               doc_max=120, scale=3.0 / math.sqrt(d))
+    slopes = alibi_slopes(4)
+    say(f"[case] fp32 mods {mask} {Nq}x{Nk} d{d}")
+    o, lse = attn_fwd(dev(c["q"], "f32"), dev(c["k"], "f32"), dev(c["v"], "f32"), scale=c["scale"], mask=mask,
+                      window=window, doc_offsets=doc_tensor(c), softcap=4.0,
+                      alibi_slopes=torch.from_numpy(slopes).cuda())
     torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(oracle.to_f64(c["q"], "f32"), oracle.to_f64(c["k"], "f32"),
+                                    oracle.to_f64(c["v"], "f32"), c["scale"], mask, window, c["doc_offsets"],
+                                    softcap=4.0, alibi_slopes=slopes.astype(np.float64))
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, F32_TOL, f"fp32 mods {mask} d{d}")
