@@ -179,7 +179,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              sink_logits: torch.Tensor | None = None, softcap: float = 0.0,
              alibi_slopes: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """Attention backward from the forward's o and lse: -> (dq, dk, dv, dsink); dsink is None
-    without sink_logits.  bf16, d = 128; dk/dv sum over each KV head's query heads."""
+    without sink_logits.  bf16, d = 64 or 128; dk/dv sum over each KV head's query heads."""
     _need(all(t.dim() == 4 for t in (q, k, v, o, do)), "q, k, v, o, do must be 4-d")
     _need(all(t.dtype == torch.bfloat16 for t in (q, k, v, o, do)), "the backward is bf16")
     _need(lse.dtype == torch.float32, "lse must be float32")

@@ -212,7 +212,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-    if (dtype != ATTN_DTYPE_BF16 || d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_DTYPE_BF16 || (d != 64 && d != 128)) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hkv * Nk == 0 && (long long)B * Hq * Nq == 0) return ATTN_OK;
     if (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr) {
@@ -250,6 +250,6 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.num_q_tiles = (int)q_tiles;
     p.num_k_tiles = (int)k_tiles;
     // with no query rows the dK/dV pass still runs and writes zeros
-    xattn::launch_backward(p, workspace, stream);
+    xattn::launch_backward(p, d, workspace, stream);
     return hip_status(hipGetLastError());
 }

@@ -1,4 +1,4 @@
-// Attention backward (bf16, head dim 128) by recomputation from the saved
+// Attention backward (bf16, head dim 64 or 128) by recomputation from the saved
 // log-sum-exp, the FlashAttention-2 backward ("Attention Is the Bottleneck",
 // FlashAttention-2 section: the forward keeps only O and the per-row
 // statistic; the backward recomputes the probabilities tile by tile).
@@ -27,13 +27,12 @@ namespace xattn {
 
 namespace {
 
-constexpr int kBD = 128;   // head dim of this build of the backward
-
 // A operand of a 32x32x16 MFMA read by rows from a row-padded tile: row
 // (lane & 31) + 32 jb, head-dim chunk 2 kk + (lane >> 5).  rl = this lane's
 // base, tile + (lane & 31) * KS * 16 + (lane >> 5) * 16.
+template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const uint8_t* rl, int jb, int kk) {
-    using C = PrefillBf16Cfg<kBD>;
+    using C = PrefillBf16Cfg<D>;
     return __builtin_bit_cast(bf16x8, *(const u32x4*)(rl + jb * 32 * C::KS * 16 + kk * 32));
 }
 
@@ -42,8 +41,9 @@ __device__ __forceinline__ bf16x8 row_operand(const uint8_t* rl, int jb, int kk)
 // kb*16 + 8 (t / 4) + 4 (lane >> 5) + t % 4, t = 0..7, the row order of the
 // B operand packed from a 32x32 accumulator's registers in order.  tl = this
 // lane's base, tile + vbase.
+template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tl, int kb, int cb) {
-    using C = PrefillBf16Cfg<kBD>;
+    using C = PrefillBf16Cfg<D>;
     const uint8_t* vp = tl + kb * 16 * C::VS * 16 + cb * 64;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
@@ -68,22 +68,24 @@ __device__ __forceinline__ void order_operand_reads() {
 
 // acc[jb] = sum_kk A(rows of the tile) x bf[kk]: a 64 x 32 product over the
 // head dim (16 MFMAs).
-__device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)[kBD / 16], f32x16 (&acc)[2]) {
+template <int D>
+__device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)[D / 16], f32x16 (&acc)[2]) {
     acc[0] = f32x16{};
     acc[1] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < kBD / 16; ++kk)
+    for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
-            acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(rl, jb, kk), bf[kk], acc[jb], 0, 0, 0);
-    order_operand_reads<kBD / 8, 1, 4>();
+            acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(rl, jb, kk), bf[kk], acc[jb], 0, 0, 0);
+    order_operand_reads<D / 8, 1, 4>();
 }
 
 // Store a d x 32 accumulator (column = this lane's row or key) as one bf16
 // row of d values, times `mul`.
-__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[kBD / 32], float mul, int lane) {
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int lane) {
 #pragma unroll
-    for (int cb = 0; cb < kBD / 32; ++cb)
+    for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             u32x2 w;
@@ -95,9 +97,10 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[kBD
 
 // The B operand fragment of a row held in registers (query row for dQ, key
 // for dK/dV): chunks (lane >> 5) * 8 .. + 8 of every 16-wide head-dim step.
-__device__ __forceinline__ void load_fragment(const uint16_t* rowp, bool ok, int lane, bf16x8 (&f)[kBD / 16]) {
+template <int D>
+__device__ __forceinline__ void load_fragment(const uint16_t* rowp, bool ok, int lane, bf16x8 (&f)[D / 16]) {
 #pragma unroll
-    for (int kk = 0; kk < kBD / 16; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk) {
         const u32x4 w = ok ? *(const u32x4*)(rowp + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
         f[kk] = __builtin_bit_cast(bf16x8, w);
     }
@@ -122,23 +125,25 @@ __global__ void bwd_zero_kernel(float* x, int n) {
     if (i < n) x[i] = 0.f;
 }
 
-// 16 threads per query row: D = dO . O over 128 columns, plus the row's
-// statistics for the two gradient passes.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) {
+// D / 8 threads per query row (8 columns each): D = dO . O, plus the row's
+// statistics for the two gradient passes.  256 / (D / 8) rows per workgroup.
+template <int D>
+__device__ __forceinline__ void bwd_prep_body(BackwardParams p) {
+    constexpr int TPR = D / 8;
     const int t = threadIdx.x;
     const long long rows = (long long)p.B * p.Hq * p.Nq;
-    const long long rg = (long long)blockIdx.x * 16 + t / 16;
+    const long long rg = (long long)blockIdx.x * (256 / TPR) + t / TPR;
     float acc = 0.f;
     if (rg < rows) {
-        const u32x4 a = *(const u32x4*)(p.o + rg * kBD + (t % 16) * 8);
-        const u32x4 g = *(const u32x4*)(p.dO + rg * kBD + (t % 16) * 8);
+        const u32x4 a = *(const u32x4*)(p.o + rg * D + (t % TPR) * 8);
+        const u32x4 g = *(const u32x4*)(p.dO + rg * D + (t % TPR) * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
     }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (rg < rows && t % 16 == 0) {
+    for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (rg < rows && t % TPR == 0) {
         const int i = (int)(rg % p.Nq);
         const int h = (int)((rg / p.Nq) % p.Hq);
         const float L = p.lse[rg];
@@ -154,18 +159,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) {
     }
 }
 
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) { bwd_prep_body<128>(p); }
+__global__ __launch_bounds__(256) void bwd_prep_d64_kernel(BackwardParams p) { bwd_prep_body<64>(p); }
+
 // dQ: per 32-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
 // dQ^T += K^T dS^T.  K is copied twice (row and transposed layouts), V once.
 // With 32-key tiles a stage of that ring is 28 KiB and a wave needs 190
 // registers, so two workgroups share a CU and two waves each SIMD (64-key
 // tiles took 54 KiB per stage and 280 registers, one wave per SIMD; the
 // backward of C2 went from 468 to 414 us with this change).
+template <int D>
 struct DqCfg {
     static constexpr int BN = 32;
-    static constexpr int KS = kBD / 8 + 1;        // row layout: one 16-byte slot of padding per row
-    static constexpr int VS = kBD / 8 + 4;        // transposed layout: four slots
-    static constexpr int KLOADS = 9;              // 32 x 17 slots = 8.5 KiB, copied as 9 KiB (two slack rows)
-    static constexpr int VLOADS = 10;             // 32 x 20 slots = 10 KiB
+    static constexpr int KS = D / 8 + 1;          // row layout: one 16-byte slot of padding per row
+    static constexpr int VS = D / 8 + 4;          // transposed layout: four slots
+    // whole 1 KiB copies, rounded up (d 128: 32 x 17 slots = 8.5 KiB copied
+    // as 9 KiB, the slack rows never read; d 64: 4.5 KiB as 5)
+    static constexpr int KLOADS = (BN * KS * 16 + 1023) / 1024;
+    static constexpr int VLOADS = (BN * VS * 16 + 1023) / 1024;
     static constexpr int KTILE = KLOADS * 1024;
     static constexpr int VTILE = VLOADS * 1024;
     static constexpr int KLW = (KLOADS + 3) / 4;
@@ -177,9 +188,9 @@ struct DqCfg {
 // P (dP - D) is with respect to t; the cap's chain-rule factor
 // dt/dx = 1 - tanh^2 = 4 r (1 - r), r = 1 / (e^(2x/c) + 1), turns it into
 // the gradient with respect to x (the slope bias does not depend on q or k).
-template <bool MODS>
+template <int D, bool MODS>
 __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
-    using C = DqCfg;
+    using C = DqCfg<D>;
     constexpr int BM = 128;
     __shared__ __attribute__((aligned(1024))) uint8_t kr0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::VTILE];
@@ -211,29 +222,29 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     const bool wave_has_rows = w0 < p.Nq;
 
     const size_t head_row = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-    bf16x8 qf[kBD / 16], df[kBD / 16];
-    load_fragment(p.q + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, qf);
-    load_fragment(p.dO + (head_row + (row_ok ? row : 0)) * kBD, row_ok, lane, df);
+    bf16x8 qf[D / 16], df[D / 16];
+    load_fragment<D>(p.q + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, qf);
+    load_fragment<D>(p.dO + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, df);
     const float nl = row_ok ? p.ws_nl[head_row + row] : -__builtin_inff();
     const float Drow = row_ok ? p.ws_d[head_row + row] : 0.f;
 
-    f32x16 acc[kBD / 32];
+    f32x16 acc[D / 32];
 #pragma unroll
-    for (int cb = 0; cb < kBD / 32; ++cb) acc[cb] = f32x16{};
+    for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
 
-    const uint16_t* kg_ = p.k + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * kBD;
-    const uint16_t* vg_ = p.v + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * kBD;
+    const uint16_t* kg_ = p.k + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
+    const uint16_t* vg_ = p.v + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
     const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, C::BN);
     uint32_t koff[C::KLW], voff[C::VLW];
-    tile_src_offsets<kBD, C::KS, C::KLOADS>(koff, wave, lane);
-    tile_src_offsets<kBD, C::VS, C::VLOADS>(voff, wave, lane);
+    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
     const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
     const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
 
     auto copy = [&](int t, uint8_t* kr, uint8_t* kt, uint8_t* vr) __attribute__((always_inline)) {
-        load_tile_async<kBD, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kr, koff, wave);
-        load_tile_async<kBD, C::VS, C::VLOADS>(kg_, t * C::BN, p.Nk, kt, voff, wave);
-        load_tile_async<kBD, C::KS, C::KLOADS>(vg_, t * C::BN, p.Nk, vr, koff, wave);
+        load_tile_async<D, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kr, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(kg_, t * C::BN, p.Nk, kt, voff, wave);
+        load_tile_async<D, C::KS, C::KLOADS>(vg_, t * C::BN, p.Nk, vr, koff, wave);
     };
     auto stage = [&](int it, const uint8_t* kr, const uint8_t* kt, const uint8_t* vr, uint8_t* krn, uint8_t* ktn,
                      uint8_t* vrn) __attribute__((always_inline)) {
@@ -249,13 +260,13 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
         const uint8_t* krl = kr + kbase;
         const uint8_t* vrl = vr + kbase;
 #pragma unroll
-        for (int kk = 0; kk < kBD / 16; ++kk) {
+        for (int kk = 0; kk < D / 16; ++kk) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, *(const u32x4*)(krl + kk * 32)), qf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, *(const u32x4*)(vrl + kk * 32)), df[kk], dp, 0, 0, 0);
         }
-        order_operand_reads<kBD / 8, 1, 4>();
+        order_operand_reads<D / 8, 1, 4>();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -290,7 +301,7 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int cb = 0; cb < kBD / 32; ++cb) {
+            for (int cb = 0; cb < D / 32; ++cb) {
                 const uint8_t* vp = ktl + kb * 16 * C::VS * 16 + cb * 64;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
@@ -298,7 +309,7 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), dsf[kb], acc[cb], 0, 0, 0);
             }
-        order_operand_reads<kBD / 16, 2, 2>();
+        order_operand_reads<D / 16, 2, 2>();
     };
 
     if (tr.n > 0) {
@@ -308,18 +319,20 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
             if (it + 1 < tr.n) stage(it + 1, kr1, kt1, vr1, kr0, kt0, vr0);
         }
     }
-    if (row_ok) store_row(p.dq + (head_row + row) * kBD, acc, p.scale, lane);
+    if (row_ok) store_row<D>(p.dq + (head_row + row) * D, acc, p.scale, lane);
 }
 
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) { bwd_dq_body<false>(p); }
-__global__ __launch_bounds__(256, 2) void bwd_dq_mod_kernel(BackwardParams p) { bwd_dq_body<true>(p); }
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) { bwd_dq_body<128, false>(p); }
+__global__ __launch_bounds__(256, 2) void bwd_dq_mod_kernel(BackwardParams p) { bwd_dq_body<128, true>(p); }
+__global__ __launch_bounds__(256, 2) void bwd_dq_d64_kernel(BackwardParams p) { bwd_dq_body<64, false>(p); }
+__global__ __launch_bounds__(256, 2) void bwd_dq_d64_mod_kernel(BackwardParams p) { bwd_dq_body<64, true>(p); }
 
 // dK and dV: each wave owns 32 keys (K and V fragments in registers) and
 // streams 64-row query tiles of every query head of its group.
 // MODS: as for the dQ pass; each streamed tile's query head brings its own slope.
-template <bool MODS>
+template <int D, bool MODS>
 __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
-    using C = PrefillBf16Cfg<kBD>;
+    using C = PrefillBf16Cfg<D>;
     constexpr int BQ = 64;    // query rows per streamed tile
     constexpr int BK = 128;   // keys per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t qr0[C::KTILE];
@@ -349,12 +362,12 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     const int k_last = min(k0 + BK, p.Nk) - 1;
 
     const size_t kv_head = ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk;
-    bf16x8 kf[kBD / 16], vf[kBD / 16];
-    load_fragment(p.k + (kv_head + (key_ok ? key : 0)) * kBD, key_ok, lane, kf);
-    load_fragment(p.v + (kv_head + (key_ok ? key : 0)) * kBD, key_ok, lane, vf);
-    f32x16 dk[kBD / 32], dv[kBD / 32];
+    bf16x8 kf[D / 16], vf[D / 16];
+    load_fragment<D>(p.k + (kv_head + (key_ok ? key : 0)) * D, key_ok, lane, kf);
+    load_fragment<D>(p.v + (kv_head + (key_ok ? key : 0)) * D, key_ok, lane, vf);
+    f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-    for (int cb = 0; cb < kBD / 32; ++cb) {
+    for (int cb = 0; cb < D / 32; ++cb) {
         dk[cb] = f32x16{};
         dv[cb] = f32x16{};
     }
@@ -392,8 +405,8 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     const int n_iter = ntq * p.group;
 
     uint32_t koff[C::KLW], voff[C::VLW];
-    tile_src_offsets<kBD, C::KS, C::KLOADS>(koff, wave, lane);
-    tile_src_offsets<kBD, C::VS, C::VLOADS>(voff, wave, lane);
+    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
     const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
     const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
 
@@ -404,12 +417,12 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         __attribute__((always_inline)) {
         const size_t head_row = ((size_t)b * p.Hq + head_of(it)) * (size_t)p.Nq;
         const int q0 = q0_of(it);
-        const uint16_t* qg = p.q + head_row * kBD;
-        const uint16_t* dg = p.dO + head_row * kBD;
-        load_tile_async<kBD, C::KS, C::KLOADS>(qg, q0, p.Nq, qr, koff, wave);
-        load_tile_async<kBD, C::VS, C::VLOADS>(qg, q0, p.Nq, qt, voff, wave);
-        load_tile_async<kBD, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
-        load_tile_async<kBD, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
+        const uint16_t* qg = p.q + head_row * D;
+        const uint16_t* dg = p.dO + head_row * D;
+        load_tile_async<D, C::KS, C::KLOADS>(qg, q0, p.Nq, qr, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(qg, q0, p.Nq, qt, voff, wave);
+        load_tile_async<D, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
         if (wave == 0) {
             const int nrow = (p.Nq - q0) * 4;   // bytes of rows that exist; the rest read 0
             const void* srcs[4] = {p.ws_nl + head_row + q0, p.ws_d + head_row + q0, p.ws_lo + head_row + q0,
@@ -438,7 +451,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         const bool full = q0 + BQ - 1 < p.Nq && k0w + 31 < p.Nk && hi_a >= k0w + 31 &&
                           (lo_z <= k0w || k0w + 31 < p.sink_end);
         f32x16 s[2], dp[2];
-        rows_times(qr + kbase, kf, s);    // S = Q K^T   (columns: this lane's key)
+        rows_times<D>(qr + kbase, kf, s);    // S = Q K^T   (columns: this lane's key)
         // MODS: S -> modified base-2 scores (before the mask: a capped -inf
         // would come back finite) and the cap factor of each element.  Element
         // (jb, r) is row q0 + 32 jb + 8 (r / 4) + 4 (lane / 32) + r % 4.
@@ -492,22 +505,24 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
             nl4[q] = *(const f32x4*)(nl + rb);
             dd4[q] = *(const f32x4*)(dd + rb);
         }
-        // dP = dO V^T, each product followed by two of the tile's 32 P = exp2(.)
+        // dP = dO V^T (NM = D / 8 products), each followed by EPM of the tile's
+        // 32 P = exp2(.)
         {
+            constexpr int NM = D / 8, EPM = 32 / NM;
             dp[0] = f32x16{};
             dp[1] = f32x16{};
             const uint8_t* drl = dr + kbase;
             bf16x8 ra[5];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = row_operand(drl, j & 1, j >> 1);
+            for (int j = 0; j < 4; ++j) ra[j] = row_operand<D>(drl, j & 1, j >> 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i + 4 < 16) ra[(i + 4) % 5] = row_operand(drl, (i + 4) & 1, (i + 4) >> 1);
+            for (int i = 0; i < NM; ++i) {
+                if (i + 4 < NM) ra[(i + 4) % 5] = row_operand<D>(drl, (i + 4) & 1, (i + 4) >> 1);
                 dp[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % 5], vf[i >> 1], dp[i & 1], 0, 0, 0);
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int el = 2 * i + x, jb = el >> 4, r = el & 15, q = 4 * jb + (r >> 2);
+                for (int x = 0; x < EPM; ++x) {
+                    const int el = EPM * i + x, jb = el >> 4, r = el & 15, q = 4 * jb + (r >> 2);
                     s[jb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], sl, nl4[q][r & 3]));   // P
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -531,12 +546,15 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
             pf[kb] = __builtin_bit_cast(bf16x8, wp);
             dsf[kb] = __builtin_bit_cast(bf16x8, wd);
         };
-        // product i: block kb = i / 8, head-dim block cb = (i / 2) % 4, dV (i even) or dK (i odd)
+        // product i: block kb = i / PPB, head-dim block cb = (i / 2) % CB, dV
+        // (i even) or dK (i odd); PPB = 2 CB products per 16-row block, each
+        // followed by EPP of the next block's 8 dS elements
+        constexpr int CB = D / 32, PPB = 2 * CB, NP = 4 * PPB, EPP = 8 / PPB;
         auto operand = [&](int i) __attribute__((always_inline)) {
-            return tr_operand(((i & 1) ? qt : dt) + vbase, i >> 3, (i >> 1) & 3);
+            return tr_operand<D>(((i & 1) ? qt : dt) + vbase, i / PPB, (i >> 1) % CB);
         };
-        // Block 0's dS first; then the 32 dV / dK products, each followed by
-        // one element of the next block's dS and the operand reads of the
+        // Block 0's dS first; then the dV / dK products, each followed by
+        // EPP elements of the next block's dS and the operand reads of the
         // product two ahead, pinned in that order by scheduling barriers.  At
         // one wave per SIMD nothing else fills the matrix core while VALU work
         // issues: with the exponentials and dS all ahead of the products (the
@@ -551,14 +569,15 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         opr[1] = operand(1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int kb = i >> 3, cb = (i >> 1) & 3;
-            if (i + 2 < 32) opr[(i + 2) % 3] = operand(i + 2);
+        for (int i = 0; i < NP; ++i) {
+            const int kb = i / PPB, cb = (i >> 1) % CB;
+            if (i + 2 < NP) opr[(i + 2) % 3] = operand(i + 2);
             if (i & 1) dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[i % 3], dsf[kb], dk[cb], 0, 0, 0);
             else dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opr[i % 3], pf[kb], dv[cb], 0, 0, 0);
             if (kb < 3) {
-                element(kb + 1, i & 7);
-                if ((i & 7) == 7) pack(kb + 1);
+#pragma unroll
+                for (int y = 0; y < EPP; ++y) element(kb + 1, (i % PPB) * EPP + y);
+                if (i % PPB == PPB - 1) pack(kb + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -572,20 +591,22 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         }
     }
     if (key_ok) {
-        store_row(p.dk + (kv_head + key) * kBD, dk, p.scale, lane);
-        store_row(p.dv + (kv_head + key) * kBD, dv, 1.f, lane);
+        store_row<D>(p.dk + (kv_head + key) * D, dk, p.scale, lane);
+        store_row<D>(p.dv + (kv_head + key) * D, dv, 1.f, lane);
     }
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) { bwd_dkdv_body<false>(p); }
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_mod_kernel(BackwardParams p) { bwd_dkdv_body<true>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) { bwd_dkdv_body<128, false>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_mod_kernel(BackwardParams p) { bwd_dkdv_body<128, true>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_kernel(BackwardParams p) { bwd_dkdv_body<64, false>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_mod_kernel(BackwardParams p) { bwd_dkdv_body<64, true>(p); }
 
 size_t backward_workspace_bytes(int B, int Hq, int Nq) {
     const size_t rows = (size_t)B * Hq * Nq;
     return 4 * ((rows * 4 + 255) / 256) * 256;
 }
 
-int launch_backward(BackwardParams p, void* ws, hipStream_t stream) {
+int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
     const size_t rows = (size_t)p.B * p.Hq * p.Nq;
     const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
     const size_t stride = ((rows * 4 + 255) / 256) * 256;
@@ -597,14 +618,28 @@ int launch_backward(BackwardParams p, void* ws, hipStream_t stream) {
     // memset, so the sequence can be captured into a graph)
     if (p.dsink != nullptr && p.Hq > 0)
         hipLaunchKernelGGL(bwd_zero_kernel, dim3((p.Hq + 255) / 256), dim3(256), 0, stream, p.dsink, p.Hq);
+    const dim3 wg(256), gq(p.B * p.Hq * p.num_q_tiles), gk(p.B * p.Hkv * p.num_k_tiles);
     if (rows > 0) {
-        hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
-        if (mods) hipLaunchKernelGGL(bwd_dq_mod_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.Hq * p.num_q_tiles), dim3(256), 0, stream, p);
+        const size_t rows_per_wg = 256 / (d / 8);   // the prep pass's D / 8 threads per row
+        const dim3 gp((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+        if (d == 128) {
+            hipLaunchKernelGGL(bwd_prep_kernel, gp, wg, 0, stream, p);
+            if (mods) hipLaunchKernelGGL(bwd_dq_mod_kernel, gq, wg, 0, stream, p);
+            else hipLaunchKernelGGL(bwd_dq_kernel, gq, wg, 0, stream, p);
+        } else {
+            hipLaunchKernelGGL(bwd_prep_d64_kernel, gp, wg, 0, stream, p);
+            if (mods) hipLaunchKernelGGL(bwd_dq_d64_mod_kernel, gq, wg, 0, stream, p);
+            else hipLaunchKernelGGL(bwd_dq_d64_kernel, gq, wg, 0, stream, p);
+        }
     }
     if ((long long)p.B * p.Hkv * p.num_k_tiles > 0) {
-        if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.Hkv * p.num_k_tiles), dim3(256), 0, stream, p);
+        if (d == 128) {
+            if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, gk, wg, 0, stream, p);
+            else hipLaunchKernelGGL(bwd_dkdv_kernel, gk, wg, 0, stream, p);
+        } else {
+            if (mods) hipLaunchKernelGGL(bwd_dkdv_d64_mod_kernel, gk, wg, 0, stream, p);
+            else hipLaunchKernelGGL(bwd_dkdv_d64_kernel, gk, wg, 0, stream, p);
+        }
     }
     return 0;
 }

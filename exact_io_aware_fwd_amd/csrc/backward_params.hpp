@@ -38,6 +38,6 @@ struct BackwardParams {
 };
 
 size_t backward_workspace_bytes(int B, int Hq, int Nq);
-int launch_backward(BackwardParams p, void* ws, hipStream_t stream);
+int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream);   // d: 64 or 128
 
 }  // namespace xattn

@@ -244,7 +244,7 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
  *                bytes, 16-byte aligned; not to be shared by concurrent calls
  *
  * Every mask kind and both sink forms apply as in attn_fwd.  This build
- * supports dtype BF16 with d = 128 (anything else: ATTN_ERR_UNSUPPORTED).
+ * supports dtype BF16 with d = 64 or 128 (anything else: ATTN_ERR_UNSUPPORTED).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* dsink,

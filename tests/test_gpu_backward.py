@@ -1,6 +1,7 @@
 """Backward pass on the GPU against the fp64 oracle's gradients: dq, dk, dv
 (and the learned sinks' gradient) after the GPU forward, over every mask kind,
-GQA, ragged sizes, rows that see nothing and both sink forms.
+GQA, ragged sizes, rows that see nothing, both sink forms, the score
+modifications and both head dims (128, and 64 in the tests at the end).
 
 Tolerance (no stated bound covers gradients; derived from the arithmetic):
 P and dS enter their products rounded to bf16 (relative 2^-9 each) and D
@@ -108,3 +109,22 @@ def test_backward_score_mods_ragged_with_sinks():
     c = workloads.make_backward(1, 8, 2, 500, 500, 128, seed=81, mask="window", window=96, scale=0.2)
     sinks = np.random.default_rng(82).normal(0.0, 2.0, 8).astype(np.float32)
     run_case(c, "bwd mods window96 sinks", 4, sinks, softcap=2.5, slopes=alibi_slopes(8))
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 70), ("document", 0)])
+def test_backward_d64_masks(mask, window):
+    c = workloads.make_backward(1, 8, 2, 520, 520, 64, seed=83, mask=mask, window=window, doc_min=60, doc_max=250)
+    run_case(c, f"bwd d64 {mask}")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(300, 200), (65, 65), (1, 130), (129, 500)])
+def test_backward_d64_ragged(Nq, Nk):
+    c = workloads.make_backward(2, 4, 4, Nq, Nk, 64, seed=85, mask="causal")
+    run_case(c, f"bwd d64 causal {Nq}x{Nk}")
+
+
+def test_backward_d64_sinks_and_mods():
+    c = workloads.make_backward(1, 8, 2, 500, 500, 64, seed=87, mask="window", window=96, scale=0.25)
+    sinks = np.random.default_rng(88).normal(0.0, 2.0, 8).astype(np.float32)
+    run_case(c, "bwd d64 window96 sinks", 4, sinks)
+    run_case(c, "bwd d64 window96 sinks + mods", 4, sinks, softcap=2.0, slopes=alibi_slopes(8))
