@@ -189,13 +189,15 @@ def gather_sequence(pages: np.ndarray, block_table_row: np.ndarray, seq_len: int
 
 
 def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
-                 seq_lens: np.ndarray, scale: float, seqs=None, dtype: str = "f64", sink_logits=None):
+                 seq_lens: np.ndarray, scale: float, seqs=None, dtype: str = "f64", sink_logits=None,
+                 softcap: float = 0.0, alibi_slopes=None):
     """One-token decode over a paged KV cache, in float64.
 
     q [S, Hq, d]; k_pages/v_pages [P, Hkv, page_size, d]; block_table
     [S, max_pages]; seq_lens [S].  The single query of a sequence is its
     newest token, so it sees every one of the sequence's ``seq_len`` cached
-    keys.  Returns o [S', Hq, d], lse [S', Hq] for the sequences ``seqs``
+    keys (so with the score modifications it sits at position seq_len - 1).
+    Returns o [S', Hq, d], lse [S', Hq] for the sequences ``seqs``
     (default: all).  With ``dtype="bf16"`` q and the pages are raw bf16 bit
     patterns, widened here one gathered sequence at a time.
     """
@@ -216,7 +218,8 @@ def paged_decode(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_
             ks, vs = from_bf16_bits(ks), from_bf16_bits(vs)
         else:
             ks, vs = ks.astype(np.float64), vs.astype(np.float64)
-        o, lse = attention(q[s][None, :, None, :], ks[None], vs[None], scale, "none", sink_logits=sink_logits)
+        o, lse = attention(q[s][None, :, None, :], ks[None], vs[None], scale, "none", sink_logits=sink_logits,
+                           softcap=softcap, alibi_slopes=alibi_slopes)
         out_o[n] = o[0, :, 0, :]
         out_l[n] = lse[0, :, 0]
     return out_o, out_l

@@ -242,3 +242,29 @@ def test_mod_backward_matches_torch_autograd():
     dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, "causal", softcap=cap, alibi_slopes=slopes)
     for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
         np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12)
+
+
+def test_paged_decode_carries_the_mods():
+    # one query per sequence at position seq_len - 1: the same as a one-token
+    # chunk of the chunked prefill, and for q = 0 the slope bias alone gives
+    # the geometric weights e^{m (j - (L - 1))}
+    c = workloads.make_decode(3, 4, 2, 8, len_min=0, len_max=40, seq_lens=[0, 17, 33], max_seq_len=40, seed=19,
+                              tail_fill="nan")
+    slopes = np.array([0.5, -0.25, 0.125, 1.0])
+    o, lse = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"], c["scale"],
+                                 dtype="bf16", softcap=1.5, alibi_slopes=slopes)
+    op, lp = oracle.paged_prefill(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                  np.arange(4), c["scale"], "causal", dtype="bf16", softcap=1.5, alibi_slopes=slopes)
+    np.testing.assert_array_equal(o, op)
+    np.testing.assert_array_equal(lse, lp)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    zq = np.zeros_like(c["q"])                    # bf16 bit patterns of 0.0
+    o0, l0 = oracle.paged_decode(zq, c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"], c["scale"],
+                                 dtype="bf16", alibi_slopes=slopes)
+    for sq in (1, 2):
+        L = int(c["seq_lens"][sq])
+        vs = oracle.from_bf16_bits(oracle.gather_sequence(c["v_pages"], c["block_table"][sq], L))
+        for h in range(4):
+            w = np.exp(slopes[h] * (np.arange(L) - (L - 1)))
+            np.testing.assert_allclose(l0[sq, h], math.log(w.sum()), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o0[sq, h], (w[:, None] * vs[h // 2]).sum(0) / w.sum(), rtol=0, atol=1e-12)
