@@ -45,7 +45,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_paged_decode_workspace_size.argtypes = [i, i, i, i]
     L.attn_paged_decode_workspace_size.restype = sz
-    L.attn_paged_decode.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, p, p, sz, p]
+    L.attn_paged_decode.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, p, f, p, p, sz, p]
     L.attn_paged_decode.restype = i
     L.attn_paged_prefill.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, AttnMask, p]
     L.attn_paged_prefill.restype = i

@@ -38,6 +38,14 @@ def _sink_ptr(sink_logits: torch.Tensor | None, Hq: int):
     return sink_logits.data_ptr()
 
 
+def _slopes_ptr(alibi_slopes: torch.Tensor | None, Hq: int):
+    if alibi_slopes is None:
+        return None
+    _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and alibi_slopes.is_contiguous()
+          and alibi_slopes.numel() == Hq, "alibi_slopes must be a contiguous float32 device tensor of Hq entries")
+    return alibi_slopes.data_ptr()
+
+
 def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
               sink_tokens: int = 0, sink_logits: torch.Tensor | None = None, Hq: int = 0,
               softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None) -> _lib.AttnMask:
@@ -48,12 +56,7 @@ def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | N
     m.sink_tokens = int(sink_tokens)
     m.sink_logits = _sink_ptr(sink_logits, Hq)
     m.softcap = float(softcap)
-    if alibi_slopes is not None:
-        _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and alibi_slopes.is_contiguous()
-              and alibi_slopes.numel() == Hq, "alibi_slopes must be a contiguous float32 device tensor of Hq entries")
-        m.alibi_slopes = alibi_slopes.data_ptr()
-    else:
-        m.alibi_slopes = None
+    m.alibi_slopes = _slopes_ptr(alibi_slopes, Hq)
     if mask == "document":
         _need(doc_offsets is not None and doc_offsets.dtype == torch.int32 and doc_offsets.is_cuda
               and doc_offsets.is_contiguous(), "document mask needs int32 device doc_offsets")
@@ -101,10 +104,12 @@ def attn_paged_decode_workspace_size(num_seqs: int, Hq: int, d: int, max_seq_len
 def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                       block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
                       scale: float | None = None, sink_logits: torch.Tensor | None = None,
+                      softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None,
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       with_lse: bool = True, stream=None):
-    """Paged decode: q [S,Hq,d], pages [P,Hkv,16,d] -> (o [S,Hq,d] bf16, lse [S,Hq] fp32)."""
+    """Paged decode: q [S,Hq,d], pages [P,Hkv,16,d] -> (o [S,Hq,d] bf16, lse [S,Hq] fp32).
+    softcap and alibi_slopes [Hq] fp32 are the optional score modifications."""
     _need(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad shapes")
     _need(q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16,
           "paged decode is bf16")
@@ -127,7 +132,8 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                       ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(out),
                                       None if lse is None else ctypes_ptr(lse),
                                       S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
-                                      float(scale), _sink_ptr(sink_logits, Hq), ctypes_ptr(workspace),
+                                      float(scale), _sink_ptr(sink_logits, Hq), float(softcap),
+                                      _slopes_ptr(alibi_slopes, Hq), ctypes_ptr(workspace),
                                       workspace.numel(), _stream(stream))
     _lib.check(st)
     return out, lse

@@ -112,12 +112,15 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
                                  void* o, float* lse,
                                  int num_seqs, int Hq, int Hkv, int d, int page_size,
                                  int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
+                                 float softcap, const float* alibi_slopes,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (num_seqs < 0 || Hq < 0 || Hkv < 0 || d < 0 || max_pages_per_seq < 0 || max_seq_len < 0)
         return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)sink_logits & 3u) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (!(softcap >= 0.f) || softcap == __builtin_inff() || ((uintptr_t)alibi_slopes & 3u) != 0)
+        return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
     if ((long long)max_pages_per_seq * page_size < max_seq_len) return ATTN_ERR_INVALID_ARGUMENT;
@@ -142,6 +145,8 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
     p.max_pages = max_pages_per_seq; p.max_splits = 0;
     p.scale_log2 = scale * xattn::kLog2e;
     p.sink_logits = sink_logits;
+    p.softcap = softcap;
+    p.alibi_slopes = alibi_slopes;
     p.ws_o = nullptr; p.ws_lse = nullptr;
     xattn::launch_decode(p, d, max_seq_len, workspace, stream);
     return hip_status(hipGetLastError());

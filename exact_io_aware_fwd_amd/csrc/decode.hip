@@ -53,7 +53,10 @@ constexpr int kRing = 4;   // pages each wave keeps in flight (registers)
 // default policy.
 constexpr int kStreamLoad = 2;
 
-template <int D>
+// MODS: the score modifications (soft cap, per-head slope times the key's
+// distance from the query at position seq_len - 1) turn each score into its
+// base-2 logit before the softmax.
+template <int D, bool MODS>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int T = kSplitTokens;
     constexpr int NM = D / 32;              // MFMA steps over the head dim = 16-byte loads per lane per page
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
             if (lane < 16) {
                 f32x4 v;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = t_in < ntok ? acc[r] * p.scale_log2 : neg_inf();
+                for (int r = 0; r < 4; ++r) v[r] = t_in < ntok ? (MODS ? acc[r] : acc[r] * p.scale_log2) : neg_inf();
                 *(f32x4*)(&scw[i * kPage + lane][0]) = v;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mloc[r] = fmaxf(mloc[r], v[r]);
@@ -189,6 +192,36 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 constexpr int k = decltype(k_tag)::value;
                 if (k < n) load_page(ring[k], p.vp, k, voff);
             });
+        }
+        // ---- score modifications: the wave's stored raw scores (register r:
+        // head hc + r) become base-2 logits, and its maxima are taken again
+        if constexpr (MODS) {
+            const ScoreMod smod = make_score_mod(p.scale_log2, p.softcap, nullptr, 0);
+            float sl2[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sl2[r] = p.alibi_slopes != nullptr && hc + r < p.group
+                             ? p.alibi_slopes[hkv * p.group + hc + r] * kLog2e : 0.f;
+                mloc[r] = neg_inf();
+            }
+            for (int t = lane; t < n * kPage; t += 64) {
+                f32x4 v = *(const f32x4*)(&scw[t][0]);
+                const int tok = tok0 + (wave + 4 * (t / kPage)) * kPage + t % kPage;
+                const float dist = (float)(tok - (len - 1));   // key position minus the query's
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x;
+                    if (smod.cap_k != 0.f) {
+                        const float rr = __builtin_amdgcn_rcpf(fast_exp2(v[r] * smod.cap_k) + 1.f);
+                        x = __builtin_fmaf(-2.f * smod.cap_l2, rr, smod.cap_l2);
+                    } else {
+                        x = v[r] * p.scale_log2;
+                    }
+                    v[r] = v[r] == neg_inf() ? neg_inf() : __builtin_fmaf(sl2[r], dist, x);
+                    mloc[r] = fmaxf(mloc[r], v[r]);
+                }
+                *(f32x4*)(&scw[t][0]) = v;
+            }
         }
         // ---- 2. this wave's own max and sum over its tokens
         float sm[4];
@@ -364,10 +397,14 @@ int launch_decode(DecodeParams p, int d, int max_seq_len, void* ws, hipStream_t 
     p.ws_lse = (float*)((char*)ws + ((rows * d * sizeof(float) + 255) / 256) * 256);
     if (max_splits > 0) {
         const int blocks = p.num_seqs * p.Hkv * p.max_splits;
-        if (d == 128)
-            hipLaunchKernelGGL(decode_split_kernel<128>, dim3(blocks), dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL(decode_split_kernel<64>, dim3(blocks), dim3(256), 0, stream, p);
+        const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
+        if (d == 128) {
+            if (mods) hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_split_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_split_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, p);
+        } else {
+            if (mods) hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_split_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_split_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, p);
+        }
     }
     const int cblocks = (p.num_seqs * p.Hq + 3) / 4;
     if (d == 128)

@@ -23,6 +23,8 @@ struct DecodeParams {
     int num_seqs, Hq, Hkv, group, max_pages, max_splits;
     float scale_log2;
     const float* sink_logits;   // [Hq] learned sink logit per query head, or null
+    float softcap;              // > 0: score -> softcap * tanh(score / softcap)
+    const float* alibi_slopes;  // [Hq] or null: score += slope * (key - (seq_len - 1))
 };
 
 size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len);

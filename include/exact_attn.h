@@ -90,9 +90,9 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  *                   aligned: s gets slope[h] * (j - pos) added, a linear
  *                   penalty on the distance from the query's position pos to
  *                   key j (pos = i + Nk - Nq, as for the causal mask).
- * Supported by attn_fwd (both dtypes), attn_paged_prefill and attn_bwd (which
- * differentiates through both: the cap contributes 1 - tanh^2 to dS).  Sink
- * logits are not modified.
+ * Supported by attn_fwd (both dtypes), attn_paged_prefill, attn_paged_decode
+ * (as two arguments of its own) and attn_bwd (which differentiates through
+ * both: the cap contributes 1 - tanh^2 to dS).  Sink logits are not modified.
  */
 typedef enum {
     ATTN_MASK_NONE = 0,
@@ -162,6 +162,8 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, int max_seq
  *   lse          [num_seqs, Hq]                          float32 natural-log LSE; may be NULL
  *   sink_logits  NULL or device float32 [Hq]: learned sink per query head
  *                (see the sinks paragraph above the mask struct)
+ *   softcap,     the score modifications, as in attn_mask (0 / NULL: off);
+ *   alibi_slopes the query's position is seq_len - 1
  *   workspace    device scratch of at least
  *                attn_paged_decode_workspace_size(num_seqs, Hq, d, max_seq_len)
  *                bytes, 16-byte aligned; its contents on entry do not matter.
@@ -178,6 +180,7 @@ int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                       void* o, float* lse,
                       int num_seqs, int Hq, int Hkv, int d, int page_size,
                       int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
+                      float softcap, const float* alibi_slopes,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -69,17 +69,19 @@ def test_fwd_empty_problems_are_noops():
 
 
 def dec(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128, page=16,
-        max_pages=4, max_len=64, scale=0.1, ws=FAKE, ws_bytes=None, sinks=None):
+        max_pages=4, max_len=64, scale=0.1, ws=FAKE, ws_bytes=None, sinks=None, softcap=0.0, alibi=None):
     if ws_bytes is None:
         ws_bytes = xa.attn_paged_decode_workspace_size(S, Hq, d, max_len)
     return _lib.lib().attn_paged_decode(q, kp, vp, bt, sl, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
-                                        scale, sinks, ws, ws_bytes, None)
+                                        scale, sinks, softcap, alibi, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(page=32), 2), (dict(d=96), 2), (dict(Hq=6, Hkv=4), 1), (dict(max_pages=3), 1),
     (dict(S=-1), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(sl=None), 1), (dict(bt=None), 1),
     (dict(kp=FAKE + 2), 1), (dict(ws_bytes=16), 3), (dict(ws=None), 3), (dict(sinks=FAKE + 1), 1),
+    (dict(softcap=-1.0), 1), (dict(softcap=float("nan")), 1), (dict(softcap=float("inf")), 1),
+    (dict(alibi=FAKE + 2), 1),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status

@@ -1,7 +1,7 @@
 """Score modifications on the GPU against the fp64 oracle: a tanh soft cap
 and ALiBi-style per-head slopes, alone and together, over every mask kind,
-with sinks, in the bf16 prefill (d 128 and 64), the chunked prefill and the
-fp32 prefill (the backward's are in the backward tests)."""
+with sinks, in the bf16 prefill (d 128 and 64), the chunked prefill, the
+paged decode and the fp32 prefill (the backward's are in the backward tests)."""
 import math
 
 import numpy as np
@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from exact_io_aware_fwd_amd import attn_fwd, attn_paged_prefill
+from exact_io_aware_fwd_amd import attn_fwd, attn_paged_decode, attn_paged_prefill
 from _gpu_helpers import BF16_SHARP_TOL, F32_TOL, compare, dev, doc_tensor, host_f64, say
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +115,39 @@ def test_fp32_prefill_score_mods(d, mask, window, Nq, Nk):
                                     oracle.to_f64(c["v"], "f32"), c["scale"], mask, window, c["doc_offsets"],
                                     softcap=4.0, alibi_slopes=slopes.astype(np.float64))
     compare(host_f64(o), host_f64(lse), o_ref, l_ref, F32_TOL, f"fp32 mods {mask} d{d}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("softcap,alibi", [(2.0, False), (0.0, True), (1.5, True)])
+def test_paged_decode_score_mods(d, softcap, alibi):
+    # lengths around the 1024-key splits and the 16-token pages, an empty
+    # sequence, GQA with a group of 4, NaN in every page tail
+    c = workloads.make_decode(8, 8, 2, d, seq_lens=[0, 1, 15, 1023, 1025, 2048, 3001, 77], max_seq_len=3001,
+                              seed=101, tail_fill="nan", scale=3.0 / math.sqrt(d))
+    slopes = alibi_slopes(8) if alibi else None
+    say(f"[case] decode mods d={d} softcap={softcap} alibi={alibi}")
+    o, lse = attn_paged_decode(dev(c["q"], "bf16"), dev(c["k_pages"], "bf16"), dev(c["v_pages"], "bf16"),
+                               torch.from_numpy(c["block_table"]).cuda(), torch.from_numpy(c["seq_lens"]).cuda(),
+                               max_seq_len=c["max_seq_len"], scale=c["scale"], softcap=softcap,
+                               alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                       c["scale"], dtype="bf16", softcap=softcap,
+                                       alibi_slopes=None if slopes is None else slopes.astype(np.float64))
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, BF16_SHARP_TOL, f"decode mods d{d}")
+
+
+def test_paged_decode_mods_with_sinks():
+    c = workloads.make_decode(5, 8, 2, 128, seq_lens=[3, 700, 1024, 2500, 40], max_seq_len=2500, seed=103,
+                              tail_fill="nan")
+    slopes, sinks = alibi_slopes(8), np.random.default_rng(104).normal(0.0, 2.0, 8).astype(np.float32)
+    say("[case] decode mods + sinks")
+    o, lse = attn_paged_decode(dev(c["q"], "bf16"), dev(c["k_pages"], "bf16"), dev(c["v_pages"], "bf16"),
+                               torch.from_numpy(c["block_table"]).cuda(), torch.from_numpy(c["seq_lens"]).cuda(),
+                               max_seq_len=c["max_seq_len"], scale=c["scale"], softcap=3.0,
+                               alibi_slopes=torch.from_numpy(slopes).cuda(), sink_logits=torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], c["seq_lens"],
+                                       c["scale"], dtype="bf16", softcap=3.0, alibi_slopes=slopes.astype(np.float64),
+                                       sink_logits=sinks.astype(np.float64))
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, BF16_SHARP_TOL, "decode mods + sinks")
