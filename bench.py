@@ -55,7 +55,7 @@ CHUNKED_CONFIG = "c6_chunked_prefill_16"
 # every kernel the counter and clock summaries cover, with the workload it runs in bench.py
 KERNEL_WORKLOADS = {
     "prefill_bf16_kernel<128, false>": PREFILL_CONFIG,
-    "decode_split_kernel<128>": DECODE_CONFIG,
+    "decode_split_kernel<128, false>": DECODE_CONFIG,
     "decode_combine_kernel<128>": DECODE_CONFIG,
     "paged_prefill_swz_kernel<false>": CHUNKED_CONFIG,
     "bwd_prep_kernel": "backward of " + PREFILL_CONFIG,
@@ -291,7 +291,7 @@ def main() -> int:
     gbs = dbytes / (dec_mean * 1e-3) / 1e9
     pkey = f"prefill_bf16_kernel<{pc['d']}, false>"
     ptraffic = measured_traffic(pkey, args.prefill_config)
-    dtraffic = measured_traffic("decode_split_kernel<128>", DECODE_CONFIG)
+    dtraffic = measured_traffic("decode_split_kernel<128, false>", DECODE_CONFIG)
 
     result = {
         "metric": "attn fwd TFLOP/s (% bf16 MFMA peak) causal prefill; paged decode HBM GB/s",
@@ -326,7 +326,7 @@ def main() -> int:
             "value": round(gbs, 1), "unit": "GB/s", "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
-                         "kernel": "decode_split_kernel<128> + decode_combine_kernel<128> (one call)"},
+                         "kernel": "decode_split_kernel<128, false> + decode_combine_kernel<128> (one call)"},
         },
     }
     if not args.no_chunked:
