@@ -128,3 +128,22 @@ def test_backward_d64_sinks_and_mods():
     sinks = np.random.default_rng(88).normal(0.0, 2.0, 8).astype(np.float32)
     run_case(c, "bwd d64 window96 sinks", 4, sinks)
     run_case(c, "bwd d64 window96 sinks + mods", 4, sinks, softcap=2.0, slopes=alibi_slopes(8))
+
+
+def test_backward_c2_full_size_sampled_heads():
+    """The backward of the 2048-token causal MHA workload (B 4, H 16, d 128)
+    in the launch configuration the benchmark times; the oracle on three
+    sampled (batch, head) pairs.  With one query head per KV head a head's
+    gradients depend on that head alone, so each sample is exact."""
+    c = workloads.make_backward(4, 16, 16, 2048, 2048, 128, seed=0, mask="causal")
+    say("[case] backward of c2 at full size, sampled heads")
+    q, k, v, do = dev(c["q"], "bf16"), dev(c["k"], "bf16"), dev(c["v"], "bf16"), dev(c["do"], "bf16")
+    o, lse = attn_fwd(q, k, v, scale=c["scale"], mask="causal")
+    dq, dk, dv, _ = attn_bwd(q, k, v, o, do, lse, scale=c["scale"], mask="causal")
+    torch.cuda.synchronize()
+    f64 = lambda a, b, h: oracle.to_f64(a[b:b + 1, h:h + 1], "bf16")
+    for b, h in [(0, 0), (1, 7), (3, 15)]:
+        ref = oracle.attention_backward(f64(c["q"], b, h), f64(c["k"], b, h), f64(c["v"], b, h), f64(c["do"], b, h),
+                                        c["scale"], "causal")
+        for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+            check_grad(host_f64(got[b:b + 1, h:h + 1]), want, f"c2 b{b} h{h} {name}")
