@@ -185,9 +185,11 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              sink_logits: torch.Tensor | None = None, softcap: float = 0.0,
              alibi_slopes: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """Attention backward from the forward's o and lse: -> (dq, dk, dv, dsink); dsink is None
-    without sink_logits.  bf16, d = 64 or 128; dk/dv sum over each KV head's query heads."""
+    without sink_logits.  bf16 or fp32 (all five tensors alike), d = 64 or 128; dk/dv sum over
+    each KV head's query heads."""
     _need(all(t.dim() == 4 for t in (q, k, v, o, do)), "q, k, v, o, do must be 4-d")
-    _need(all(t.dtype == torch.bfloat16 for t in (q, k, v, o, do)), "the backward is bf16")
+    _need(all(t.dtype == q.dtype for t in (k, v, o, do)) and q.dtype in (torch.bfloat16, torch.float32),
+          "q, k, v, o, do must all be bf16 or all float32")
     _need(lse.dtype == torch.float32, "lse must be float32")
     _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v, o, do, lse)), "inputs must be contiguous device tensors")
     B, Hq, Nq, d = q.shape
@@ -204,6 +206,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     st = _lib.lib().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o), ctypes_ptr(do),
                              ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk), ctypes_ptr(dv),
                              None if dsink is None else ctypes_ptr(dsink), B, Hq, Hkv, Nq, Nk, d, float(scale), m,
-                             _lib.ATTN_DTYPE_BF16, ctypes_ptr(workspace), workspace.numel(), _stream(stream))
+                             _lib.ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else _lib.ATTN_DTYPE_F32,
+                             ctypes_ptr(workspace), workspace.numel(), _stream(stream))
     _lib.check(st)
     return dq, dk, dv, dsink

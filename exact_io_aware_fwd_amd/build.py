@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libexact_attn.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "backward_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -217,7 +217,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-    if (dtype != ATTN_DTYPE_BF16 || (d != 64 && d != 128)) return ATTN_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hkv * Nk == 0 && (long long)B * Hq * Nq == 0) return ATTN_OK;
     if (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr) {
@@ -234,6 +234,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     const long long q_tiles = (Nq + 127) / 128, k_tiles = (Nk + 127) / 128;
     if ((long long)B * Hq * q_tiles > kMaxGrid || (long long)B * Hkv * k_tiles > kMaxGrid ||
         (long long)B * Hq * Nq / 16 > kMaxGrid)
+        return ATTN_ERR_UNSUPPORTED;
+    // the fp32 passes take one wave per row and per key
+    if (dtype == ATTN_DTYPE_F32 && ((long long)B * Hq * Nq / 4 > kMaxGrid || (long long)B * Hkv * Nk / 4 > kMaxGrid))
         return ATTN_ERR_UNSUPPORTED;
 
     xattn::BackwardParams p;
@@ -255,6 +258,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.num_q_tiles = (int)q_tiles;
     p.num_k_tiles = (int)k_tiles;
     // with no query rows the dK/dV pass still runs and writes zeros
-    xattn::launch_backward(p, d, workspace, stream);
+    if (dtype == ATTN_DTYPE_BF16) xattn::launch_backward(p, d, workspace, stream);
+    else xattn::launch_backward_f32(p, d, workspace, stream);
     return hip_status(hipGetLastError());
 }

@@ -39,5 +39,6 @@ struct BackwardParams {
 
 size_t backward_workspace_bytes(int B, int Hq, int Nq);
 int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream);   // d: 64 or 128
+int launch_backward_f32(BackwardParams p, int d, void* ws, hipStream_t stream);   // fp32 tensors, same workspace
 
 }  // namespace xattn

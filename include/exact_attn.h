@@ -247,7 +247,9 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Nq);
  *                bytes, 16-byte aligned; not to be shared by concurrent calls
  *
  * Every mask kind and both sink forms apply as in attn_fwd.  This build
- * supports dtype BF16 with d = 64 or 128 (anything else: ATTN_ERR_UNSUPPORTED).
+ * supports d = 64 or 128 (else ATTN_ERR_UNSUPPORTED) with dtype BF16 (the fast
+ * path) or F32 (a full-precision checking path; every tensor above that is
+ * "bf16" is then float32, gradients included).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* dsink,

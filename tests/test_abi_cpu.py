@@ -139,7 +139,7 @@ def bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=96), 2), (dict(dtype=0), 2), (dict(dtype=5), 1), (dict(Hq=6, Hkv=4), 1), (dict(B=-1), 1),
+    (dict(d=96), 2), (dict(d=96, dtype=0), 2), (dict(dtype=5), 1), (dict(Hq=6, Hkv=4), 1), (dict(B=-1), 1),
     (dict(scale=0.0), 1), (dict(kind=9), 1), (dict(kind=2, window=0), 1), (dict(kind=1, sink_tokens=3), 1),
     (dict(q=None), 1), (dict(do=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(dq=FAKE + 8), 1),
     (dict(lse=FAKE + 2), 1), (dict(ws_bytes=8), 3), (dict(ws=None), 3), (dict(Nk=1 << 29), 2),

@@ -147,3 +147,43 @@ def test_backward_c2_full_size_sampled_heads():
                                         c["scale"], "causal")
         for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
             check_grad(host_f64(got[b:b + 1, h:h + 1]), want, f"c2 b{b} h{h} {name}")
+
+
+# fp32 checking path: inputs, outputs and gradients in float32.  Bound derived
+# for fp32 accumulation over a few hundred terms (about 1e-6 relative in
+# practice): relative Frobenius 2e-5, every element within 1e-4 x max|reference|.
+def run_case_f32(c, label, sink_tokens=0, sinks=None, softcap=0.0, slopes=None):
+    say(f"[case] {label} fp32 Nq={c['Nq']} Nk={c['Nk']} d={c['d']} mask={c['mask']} window={c['window']}")
+    q, k, v, do = (dev(c[x], "f32") for x in ("q", "k", "v", "do"))
+    kw = dict(scale=c["scale"], mask=c["mask"], window=c["window"], doc_offsets=doc_tensor(c),
+              sink_tokens=sink_tokens, sink_logits=None if sinks is None else torch.from_numpy(sinks).cuda(),
+              softcap=softcap, alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda())
+    o, lse = attn_fwd(q, k, v, **kw)
+    dq, dk, dv, ds = attn_bwd(q, k, v, o, do, lse, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(*(oracle.to_f64(c[x], "f32") for x in ("q", "k", "v", "do")), c["scale"],
+                                    c["mask"], c["window"], c["doc_offsets"], sink_tokens,
+                                    None if sinks is None else sinks.astype(np.float64), softcap=softcap,
+                                    alibi_slopes=None if slopes is None else slopes.astype(np.float64))
+    got = [host_f64(dq), host_f64(dk), host_f64(dv)] + ([host_f64(ds)] if sinks is not None else [])
+    for name, g, w in zip(("dq", "dk", "dv", "dsink"), got, ref):
+        fro = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+        mx = float(np.abs(g - w).max())
+        say(f"[grad] {label} fp32 {name}: rel-fro {fro:.3e} max-abs {mx:.3e}")
+        assert np.all(np.isfinite(g)) and fro <= 2e-5 and mx <= 1e-4 * float(np.abs(w).max()), f"{label} {name}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 50), ("document", 0)])
+def test_backward_f32(d, mask, window):
+    c = workloads.make_backward(1, 4, 2, 200, 200, d, dtype="f32", seed=89, mask=mask, window=window,
+                                doc_min=30, doc_max=90)
+    run_case_f32(c, f"bwd {mask} d{d}")
+
+
+def test_backward_f32_ragged_sinks_and_mods():
+    c = workloads.make_backward(2, 4, 2, 150, 100, 128, dtype="f32", seed=91, mask="causal")
+    run_case_f32(c, "bwd causal 150x100")          # Nq > Nk: the first rows see no key
+    c = workloads.make_backward(1, 4, 2, 220, 220, 64, dtype="f32", seed=93, mask="window", window=40, scale=0.3)
+    sinks = np.array([0.5, -1.0, 2.0, 0.0], dtype=np.float32)
+    run_case_f32(c, "bwd window sinks + mods", 3, sinks, softcap=2.0, slopes=alibi_slopes(4))
