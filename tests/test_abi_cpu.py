@@ -154,3 +154,13 @@ def test_bwd_workspace_size():
     assert xa.attn_bwd_workspace_size(2, 4, 100) == 4 * (((2 * 4 * 100 * 4) + 255) // 256) * 256
     assert xa.attn_bwd_workspace_size(-1, 4, 100) == 0
     assert bwd(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, B=0) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    # no fallback: with the shared library absent the binding raises
+    monkeypatch.setattr(_lib, "LIB_PATH", _lib.LIB_PATH + ".absent")
+    monkeypatch.setattr(_lib, "_lib", None)          # the cached handle
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        xa.status_string(0)
