@@ -30,6 +30,26 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _check_buffer(t: torch.Tensor, name: str, shape, dtype, device):
+    """A caller-supplied output or scratch tensor must be exactly what the
+    kernels write: the library sees only a pointer and cannot check it."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.device == device, f"{name} must be on {device}, got {t.device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _workspace_bytes(ws: torch.Tensor, device) -> int:
+    _need(isinstance(ws, torch.Tensor) and ws.device == device and ws.is_contiguous(),
+          f"workspace must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
+
+
+def _same_device(device, *ts):
+    _need(all(t.device == device for t in ts), f"every tensor must be on {device}")
+
+
 def _sink_ptr(sink_logits: torch.Tensor | None, Hq: int):
     if sink_logits is None:
         return None
@@ -83,12 +103,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     _need(k.shape == v.shape and k.shape[0] == B and k.shape[3] == d, "k/v shape mismatch")
+    _same_device(q.device, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                              None if lse is None else ctypes_ptr(lse),
@@ -119,22 +144,28 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
     S, Hq, d = q.shape
     _, Hkv, page_size, _ = k_pages.shape
     _need(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,), "index shapes")
+    _same_device(q.device, k_pages, v_pages, block_table, seq_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = attn_paged_decode_workspace_size(S, Hq, d, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _workspace_bytes(workspace, q.device)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if lse is None and with_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buffer(lse, "lse", (S, Hq), torch.float32, q.device)
     st = _lib.lib().attn_paged_decode(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
                                       ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(out),
                                       None if lse is None else ctypes_ptr(lse),
                                       S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
                                       float(scale), _sink_ptr(sink_logits, Hq), float(softcap),
                                       _slopes_ptr(alibi_slopes, Hq), ctypes_ptr(workspace),
-                                      workspace.numel(), _stream(stream))
+                                      ws_bytes, _stream(stream))
     _lib.check(st)
     return out, lse
 
@@ -159,12 +190,17 @@ def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
     _, Hkv, page_size, _ = k_pages.shape
     S = seq_lens.shape[0]
     _need(block_table.dim() == 2 and block_table.shape[0] == S and q_offsets.shape == (S + 1,), "index shapes")
+    _same_device(q.device, k_pages, v_pages, block_table, seq_lens, q_offsets)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if lse is None and with_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buffer(lse, "lse", (T, Hq), torch.float32, q.device)
     m = make_mask(mask, window, None, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_paged_prefill(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
                                        ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(q_offsets),
@@ -195,6 +231,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     _need(o.shape == q.shape and do.shape == q.shape and lse.shape == (B, Hq, Nq) and v.shape == k.shape, "shapes")
+    _same_device(q.device, k, v, o, do, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -202,11 +239,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     need = attn_bwd_workspace_size(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = _workspace_bytes(workspace, q.device)
     m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
     st = _lib.lib().attn_bwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(o), ctypes_ptr(do),
                              ctypes_ptr(lse), ctypes_ptr(dq), ctypes_ptr(dk), ctypes_ptr(dv),
                              None if dsink is None else ctypes_ptr(dsink), B, Hq, Hkv, Nq, Nk, d, float(scale), m,
                              _lib.ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else _lib.ATTN_DTYPE_F32,
-                             ctypes_ptr(workspace), workspace.numel(), _stream(stream))
+                             ctypes_ptr(workspace), ws_bytes, _stream(stream))
     _lib.check(st)
     return dq, dk, dv, dsink

@@ -142,7 +142,7 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
     p.block_table = block_table; p.seq_lens = seq_lens;
     p.o = (uint16_t*)o; p.lse = lse;
     p.num_seqs = num_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
-    p.max_pages = max_pages_per_seq; p.max_splits = 0;
+    p.max_pages = max_pages_per_seq; p.max_splits = 0; p.max_len = max_seq_len;
     p.scale_log2 = scale * xattn::kLog2e;
     p.sink_logits = sink_logits;
     p.softcap = softcap;
@@ -187,6 +187,7 @@ extern "C" int attn_paged_prefill(const void* q, const void* k_pages, const void
     p.o = (uint16_t*)o; p.lse = lse;
     p.num_seqs = num_seqs; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
     p.max_pages = max_pages_per_seq;
+    p.max_len = max_seq_len;
     p.num_q_tiles = (int)tiles;
     p.scale_log2 = scale * xattn::kLog2e;
     p.mask_kind = mask.kind;

@@ -424,7 +424,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         load_tile_async<D, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
         load_tile_async<D, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
         if (wave == 0) {
-            const int nrow = (p.Nq - q0) * 4;   // bytes of rows that exist; the rest read 0
+            const int nrow = min(p.Nq - q0, BQ) * 4;   // bytes of the tile's rows that exist; the rest read 0
             const void* srcs[4] = {p.ws_nl + head_row + q0, p.ws_d + head_row + q0, p.ws_lo + head_row + q0,
                                    p.ws_hi + head_row + q0};
 #pragma unroll

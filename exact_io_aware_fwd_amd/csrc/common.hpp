@@ -57,6 +57,7 @@ struct PagedPrefillParams {
     uint16_t* o;
     float* lse;                 // [total_q, Hq] or null
     int num_seqs, Hq, Hkv, group, max_pages;
+    int max_len;                // max_seq_len: seq_lens entries are clamped to [0, max_len] before use
     int num_q_tiles;            // query tiles of the longest chunk
     float scale_log2;
     int mask_kind;              // none, causal or window

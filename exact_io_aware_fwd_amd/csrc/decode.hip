@@ -13,17 +13,22 @@
 // kSplitTokens keys).  Workgroup ids run over the KV heads fastest, so the 8
 // heads' 4 KiB chunks of a page, which sit side by side in memory, are fetched
 // at about the same time.  Wave w takes pages w, w+4, ... of the split and
-// streams them HBM -> LDS through its own ring of kRing page slots
-// (buffer_load ... lds, no registers held per page), so each wave keeps 16 KiB
-// in flight with only wave-local waits.  The query heads that share the KV
-// head (GQA) are handled four at a time, so each K/V byte serves four rows.
-//   1. scores: Q'K^T on the matrix cores (v_mfma_f32_16x16x32_bf16), with the
-//      four query heads replicated over the 16 MFMA rows so every lane ends up
-//      holding all four heads' scores for its token; scaled to base 2 and
-//      parked in the wave's LDS rows (slots past the sequence end are -inf);
+// loads them straight from HBM into registers: a ring of kRing page slots
+// (each 1 KiB of a page per load instruction, range-limited buffer loads
+// with the nontemporal bit), so each wave keeps kRing pages in flight with
+// only wave-local waits.  In a full split the wave's K pages and then its V
+// pages form one load stream.  The query heads that share the KV head (GQA)
+// are handled four at a time, so each K/V byte serves four rows.
+//   1. scores: each K page passes from its ring slot through a small swizzled
+//      LDS stage of the wave into the matrix-core operand layout; Q'K^T on
+//      the matrix cores (v_mfma_f32_16x16x32_bf16), with the four query heads
+//      replicated over the 16 MFMA rows so every lane ends up holding all
+//      four heads' scores for its token; scaled to base 2 and parked in the
+//      wave's LDS rows (slots past the sequence end are -inf);
 //   2. the wave's exact max and sum over its own tokens (no online rescaling);
 //      the V copies are already in flight;
-//   3. P.V on the vector ALUs, 8 head-dim columns x 4 heads per lane;
+//   3. P.V on the vector ALUs from the V pages in the ring, 8 head-dim
+//      columns x 4 heads per lane;
 //   4. the four waves' partials are merged by log-sum-exp and the split's
 //      normalised output and base-2 log-sum-exp go to the workspace.
 // decode_combine: per (sequence, query head), merge the splits' partials.
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     // not two; the empty asm keeps the load ahead of the early exit.
     static_assert(T / kPage <= 64, "one block-table entry per lane");
     const int bt_lane = p.block_table[(size_t)s * p.max_pages + min(page0 + lane, p.max_pages - 1)];
-    const int len = p.seq_lens[s];
+    const int len = clamped_len(p, s);
     asm volatile("" ::"v"(bt_lane));
     if (tok0 >= len) return;
     const int ntok = min(T, len - tok0);
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int pair = blockIdx.x * 4 + wave;
     if (pair >= p.num_seqs * p.Hq) return;
     const int s = pair / p.Hq;
-    const int len = p.seq_lens[s];
+    const int len = clamped_len(p, s);
     const int ns = (len + kSplitTokens - 1) / kSplitTokens;
     uint16_t* orow = p.o + (size_t)pair * D;
     // a learned per-head sink joins the merge as one more split with a zero
@@ -392,6 +397,7 @@ size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len) {
 int launch_decode(DecodeParams p, int d, int max_seq_len, void* ws, hipStream_t stream) {
     const int max_splits = (max_seq_len + kSplitTokens - 1) / kSplitTokens;
     p.max_splits = max_splits > 0 ? max_splits : 1;
+    p.max_len = max_seq_len;
     const size_t rows = (size_t)p.num_seqs * p.Hq * p.max_splits;
     p.ws_o = (float*)ws;
     p.ws_lse = (float*)((char*)ws + ((rows * d * sizeof(float) + 255) / 256) * 256);

@@ -21,11 +21,22 @@ struct DecodeParams {
     float* ws_o;     // [num_seqs, Hq, max_splits, d]
     float* ws_lse;   // [num_seqs, Hq, max_splits], base-2 log-sum-exp
     int num_seqs, Hq, Hkv, group, max_pages, max_splits;
+    int max_len;     // max_seq_len: every seq_lens entry is clamped to [0, max_len] before use, so the
+                     // splits and the combine stay inside the table row and the workspace
     float scale_log2;
     const float* sink_logits;   // [Hq] learned sink logit per query head, or null
     float softcap;              // > 0: score -> softcap * tanh(score / softcap)
     const float* alibi_slopes;  // [Hq] or null: score += slope * (key - (seq_len - 1))
 };
+
+// A sequence length as the kernels use it: the caller promises
+// 0 <= seq_lens[s] <= max_seq_len; the clamp keeps a broken promise inside
+// the block-table row and the workspace (the result is then defined by the
+// clamped length, not an out-of-bounds read).
+__device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
+    const int len = p.seq_lens[s];
+    return len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+}
 
 size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len);
 int launch_decode(DecodeParams p, int d, int max_seq_len, void* ws, hipStream_t stream);

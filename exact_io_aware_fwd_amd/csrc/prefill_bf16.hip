@@ -519,7 +519,7 @@ __device__ __forceinline__ void paged_prefill_bf16_body(PagedPrefillParams pp) {
     const ScoreMod sm = MODS ? make_score_mod(pp.scale_log2, pp.softcap, pp.alibi_slopes, hq) : ScoreMod{};
     const int q0 = pp.q_offsets[seq];
     const int nq = pp.q_offsets[seq + 1] - q0;   // chunk length
-    const int L = pp.seq_lens[seq];              // cached keys, the chunk included
+    const int L = min(max(pp.seq_lens[seq], 0), pp.max_len);   // cached keys, the chunk included
     const int r0 = qt * C::BM;
     if (r0 >= nq) return;                        // whole workgroup: this chunk is shorter
 
@@ -691,7 +691,7 @@ __device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
     // (tile ranges, the per-page buffer resources) stays in scalar registers
     const int q0 = __builtin_amdgcn_readfirstlane(pp.q_offsets[seq]);
     const int nq = __builtin_amdgcn_readfirstlane(pp.q_offsets[seq + 1]) - q0;   // chunk length
-    const int L = __builtin_amdgcn_readfirstlane(pp.seq_lens[seq]);              // cached keys, the chunk included
+    const int L = __builtin_amdgcn_readfirstlane(min(max(pp.seq_lens[seq], 0), pp.max_len));   // cached keys, the chunk included
     const int r0 = qt * C::BM;
     if (r0 >= nq) return;                        // whole workgroup: this chunk is shorter
 

@@ -51,18 +51,40 @@ __device__ __forceinline__ void tile_src_offsets(uint32_t (&off)[(NL + 3) / 4], 
     }
 }
 
+// Byte range of a tile's buffer resource: the rows that exist from the
+// tile's first row on (rows = Nk - n0, possibly <= 0), but never more than the
+// tile's own `tile_rows`, so the 32-bit range cannot overflow however long the
+// sequence is (rows * D * 2 would pass 2^31 at 2^23 rows of d = 128).
+template <int D>
+__host__ __device__ constexpr uint32_t tile_range_bytes(int rows, int tile_rows) {
+    return (uint32_t)(rows <= 0 ? 0 : (rows < tile_rows ? rows : tile_rows)) * (uint32_t)(D * 2);
+}
+
+// The range arithmetic near and past the old 32-bit overflow (2^23 and 2^24
+// rows of d = 128), at the largest accepted length (2^28) and for a tile past
+// the end, checked at every build.
+static_assert(tile_range_bytes<128>((1 << 23) - 1, 64) == 64u * 256u, "range at 2^23 - 1 rows");
+static_assert(tile_range_bytes<128>(1 << 23, 64) == 64u * 256u, "range at 2^23 rows");
+static_assert(tile_range_bytes<128>(1 << 24, 64) == 64u * 256u, "range at 2^24 rows");
+static_assert(tile_range_bytes<128>(1 << 28, 64) == 64u * 256u, "range at 2^28 rows");
+static_assert(tile_range_bytes<128>(37, 64) == 37u * 256u, "a ragged last tile");
+static_assert(tile_range_bytes<64>(64, 64) == 64u * 128u, "an exact tile, d = 64");
+static_assert(tile_range_bytes<128>(0, 64) == 0u && tile_range_bytes<128>(-5, 64) == 0u, "no rows");
+
 // Issue this wave's share of the direct HBM -> LDS copies of one tile
 // (buffer_load_dwordx4 ... lds).  The buffer resource starts at key n0 and
-// covers only the keys that exist, so rows past Nk read as zeros.
+// covers only the keys that exist, so rows past Nk read as zeros.  The NL
+// 1 KiB copies of rows padded to S 16-byte slots reach ceil(NL * 64 / S) rows
+// (a tile that is not a whole number of copies fetches a few rows past its
+// end, which nothing reads back).
 template <int D, int S, int NL>
 __device__ __forceinline__ void load_tile_async(const uint16_t* __restrict__ base, int n0, int Nk, uint8_t* lds,
                                                 const uint32_t (&off)[(NL + 3) / 4], int wave) {
     // the host pass instantiates kernel templates too, and the buffer
     // resource type and builtins exist only for the device target
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int rows = Nk - n0;
     __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (size_t)n0 * D), (short)0, rows * D * 2, 0x00020000);
+        (void*)(base + (size_t)n0 * D), (short)0, (int)tile_range_bytes<D>(Nk - n0, (NL * 64 + S - 1) / S), 0x00020000);
 #pragma unroll
     for (int j = 0; j < (NL + 3) / 4; ++j) {
         const int blk = wave + 4 * j;

@@ -172,8 +172,11 @@ size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, int max_seq
  * slots past seq_len are never read into the result (they may hold any bit
  * pattern, NaN included).  A sequence with seq_len = 0 gets O = 0 and
  * LSE = -inf.  page_size must be 16, d must be 128 or 64, Hq a multiple of
- * Hkv, max_pages_per_seq * page_size >= max_seq_len.  The workspace must not
- * be shared by calls that may run concurrently.
+ * Hkv, max_pages_per_seq * page_size >= max_seq_len.  A seq_lens entry
+ * outside [0, max_seq_len] breaks the caller contract; the kernels clamp it
+ * to that range, so nothing is read outside the block-table row or the
+ * workspace (the result is then that of the clamped length).  The workspace
+ * must not be shared by calls that may run concurrently.
  */
 int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, const int32_t* seq_lens,
@@ -211,7 +214,10 @@ int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
  * no visible key (a chunk longer than its cache, seq_len = 0) get O = 0 and
  * LSE = -inf.  Caller contract (not checked, like all device-resident index
  * data): Nq_s <= max_q_len, seq_lens[s] <= max_seq_len <= max_pages_per_seq *
- * page_size.  page_size must be 16, d 128 or 64, Hq a multiple of Hkv.
+ * page_size.  A seq_lens entry outside [0, max_seq_len] is clamped to that
+ * range, so the block-table reads stay inside the sequence's row; rows of a
+ * chunk past max_q_len are not written.  page_size must be 16, d 128 or 64,
+ * Hq a multiple of Hkv.
  */
 int attn_paged_prefill(const void* q, const void* k_pages, const void* v_pages,
                        const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_offsets,

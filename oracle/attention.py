@@ -38,8 +38,12 @@ Readings of points the pages leave open (kept identical in the kernels):
 
 Parity pins: see tests/test_oracle_pins.py (brute force in 50-digit
 arithmetic, closed forms, invariants, reductions and the worked example the
-page prints for the online-softmax recurrence).  No function here is
-"parity unpinned".
+page prints for the online-softmax recurrence).  The two bf16 helpers are
+pinned there too: ``from_bf16_bits`` on all 65,536 bit patterns against
+torch's own bf16 widening and against hand-decoded patterns, and
+``round_to_bf16`` against torch's float32 -> bf16 rounding and against
+ties and near-ties that a double rounding through float32 would get wrong.
+No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -52,6 +56,26 @@ def from_bf16_bits(bits: np.ndarray) -> np.ndarray:
     """Widen raw bf16 bit patterns (uint16) exactly to float64."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), as float64.
+
+    bf16 keeps 8 significant bits and float32's exponent range.  A finite x
+    is m * 2**e with 0.5 <= |m| < 1 (frexp); m * 2**8 is then exact in
+    float64 and rint (ties to even) rounds it to the 8-bit significand.  Below
+    the smallest normal (2**-126) the spacing stays at 2**-133.  Magnitudes
+    from the largest finite bf16 value plus half its spacing up round to
+    infinity.  This rounds once, straight from float64: going through float32
+    first could round twice.  NaN and infinities pass through.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)                   # below 2**-126 the spacing is fixed at 2**-133
+    out = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    big = (2.0 - 2.0 ** -8) * 2.0 ** 127       # halfway between the largest finite value and the next binade
+    out = np.where(np.abs(x) >= big, np.copysign(np.inf, x), out)
+    return np.where(np.isfinite(x), out, x)
 
 
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:

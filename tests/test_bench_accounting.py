@@ -49,3 +49,34 @@ def test_chunked_visible_pairs_closed_form():
     L = c["seq_lens"].astype(np.int64)
     assert bench.chunked_visible_pairs(c) == int(np.sum(n * (L - n) + n * (n + 1) // 2))
     assert bench.chunked_flops(c) == 4 * 128 * 32 * bench.chunked_visible_pairs(c)
+
+
+def test_pmc_plan_maps_dispatches_to_workloads():
+    """A dispatch's workload follows from its kernel and its rank among that
+    kernel's dispatches in the counter pass; other kernels are ignored and a
+    count that does not match the plan is an error."""
+    per = {}
+    did = 0
+    names = {"prefill_bf16_kernel<128, false>": "void xattn::prefill_bf16_kernel<128, false>(xattn::PrefillParams)",
+             "decode_split_kernel<128, false>": "void xattn::decode_split_kernel<128, false>(xattn::DecodeParams)",
+             "decode_combine_kernel<128>": "void xattn::decode_combine_kernel<128>(xattn::DecodeParams)",
+             "paged_prefill_swz_kernel<false>": "void xattn::paged_prefill_swz_kernel<false>(xattn::PagedPrefillParams)",
+             "bwd_prep_kernel": "void xattn::bwd_prep_kernel(xattn::BwdParams)",
+             "bwd_dq_kernel": "void xattn::bwd_dq_kernel(xattn::BwdParams)",
+             "bwd_dkdv_kernel": "void xattn::bwd_dkdv_kernel(xattn::BwdParams)"}
+    per[(str(did), "__amd_rocclr_copyBuffer")] = 1.0
+    for leg, n in bench.PMC_PLAN:
+        for i in range(n):
+            for k in bench.LEG_KERNELS[leg]:
+                did += 1
+                per[(str(did), names[k])] = float(100 * did)
+                did += 1
+                per[(str(did), "void at::native::elementwise_kernel<...>(int)")] = -1.0
+    got = bench._by_leg(per)
+    assert set(got) == {leg for leg, _ in bench.PMC_PLAN}
+    assert len(got["c3a"]["prefill_bf16_kernel<128, false>"]) == 2
+    assert got["c2"]["prefill_bf16_kernel<128, false>"][0] == 100.0     # the first dispatch of the pass
+    assert all(v > 0 for leg in got.values() for vals in leg.values() for v in vals)
+    del per[max(per, key=lambda k: int(k[0]) if "bwd_dkdv" in k[1] else -1)]
+    with pytest.raises(SystemExit):
+        bench._by_leg(per)

@@ -8,7 +8,7 @@ import torch
 import oracle
 import workloads
 from exact_io_aware_fwd_amd import attn_fwd, attn_paged_prefill
-from _gpu_helpers import BF16_TOL, compare, dev, host_f64, say
+from _gpu_helpers import BF16_TOL, compare, dev, host_f64, parallel_map, say
 
 pytestmark = pytest.mark.gpu
 
@@ -103,23 +103,36 @@ def test_chunked_page_permutation_invariance():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-def test_chunked_full_workload_sampled_rows():
+@pytest.mark.slow
+def test_chunked_full_workload_all_rows():
     """The 16-sequence workload at full size, in the launch configuration the
-    benchmark times; the oracle recomputes a seeded sample of rows of every
-    sequence (first and last rows of each chunk plus random rows)."""
+    benchmark times; every row of every chunk and head is compared with the
+    oracle, one (sequence, query head) per host thread: each sequence is an
+    attention problem of its own with Nq = chunk, Nk = cached length, and
+    query head h reads KV head h // (Hq / Hkv)."""
     c = workloads.chunked_config("c6_chunked_prefill_16")
+    say(f"[case] c6 S={c['num_seqs']} Hq={c['Hq']} Hkv={c['Hkv']} chunk tokens={int(c['q_offsets'][-1])} "
+        f"cached={int(c['seq_lens'].sum())}")
     o, lse = run(c)
     og, lg = host_f64(o), host_f64(lse)
-    rng = np.random.default_rng(41)
-    errs = []
-    for s in range(c["num_seqs"]):
-        a, b, L = int(c["q_offsets"][s]), int(c["q_offsets"][s + 1]), int(c["seq_lens"][s])
-        n = b - a
-        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 24)]))
-        k = oracle.from_bf16_bits(oracle.gather_sequence(c["k_pages"], c["block_table"][s], L))[None]
-        v = oracle.from_bf16_bits(oracle.gather_sequence(c["v_pages"], c["block_table"][s], L))[None]
-        q = np.transpose(oracle.to_f64(c["q"][a:b], "bf16"), (1, 0, 2))[None]
-        o_ref, l_ref = oracle.attention(q, k, v, c["scale"], "causal", rows=rows)
-        errs.append(compare(og[a + rows].transpose(1, 0, 2), lg[a + rows].T, o_ref[0], l_ref[0], BF16_TOL,
-                            f"c6 seq {s} ({rows.size} rows)"))
-    say(f"[c6] worst max-abs {max(e['max_abs'] for e in errs):.3e}")
+    S, Hq, g = c["num_seqs"], c["Hq"], c["Hq"] // c["Hkv"]
+    offs, lens = c["q_offsets"], c["seq_lens"]
+    kv = parallel_map(lambda s: (oracle.from_bf16_bits(oracle.gather_sequence(c["k_pages"], c["block_table"][s],
+                                                                              int(lens[s]))),
+                                 oracle.from_bf16_bits(oracle.gather_sequence(c["v_pages"], c["block_table"][s],
+                                                                              int(lens[s])))),
+                      range(S), "c6 gather")
+    o_ref = np.empty_like(og)
+    l_ref = np.empty_like(lg)
+
+    def one(task):
+        s, h = task
+        a, b = int(offs[s]), int(offs[s + 1])
+        q = np.transpose(oracle.to_f64(c["q"][a:b, h:h + 1], "bf16"), (1, 0, 2))[None]     # [1, 1, n, d]
+        k, v = kv[s][0][h // g:h // g + 1][None], kv[s][1][h // g:h // g + 1][None]
+        ob, lb = oracle.attention(q, k, v, c["scale"], "causal")
+        o_ref[a:b, h], l_ref[a:b, h] = ob[0, 0], lb[0, 0]
+
+    work = lambda t: -(int(offs[t[0] + 1]) - int(offs[t[0]])) * int(lens[t[0]])
+    parallel_map(one, sorted(((s, h) for s in range(S) for h in range(Hq)), key=work), "c6")
+    compare(og, lg, o_ref, l_ref, BF16_TOL, f"c6 all {int(offs[-1])} rows of {Hq} heads")

@@ -7,7 +7,7 @@ import torch
 import oracle
 import workloads
 from exact_io_aware_fwd_amd import attn_paged_decode, attn_paged_decode_workspace_size
-from _gpu_helpers import BF16_TOL, compare, dev, host_f64, say
+from _gpu_helpers import BF16_TOL, compare, dev, host_f64, parallel_map, say
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +80,65 @@ def test_decode_workspace_contents_and_determinism():
 
 
 @pytest.mark.slow
-def test_config_paged_decode_64():
+def test_config_paged_decode_64_all_sequences():
+    """All 64 sequences of the decode workload, in the launch configuration
+    the benchmark times; the oracle takes one sequence per host thread."""
     c = workloads.decode_config("c5_paged_decode_64")
-    lens = c["seq_lens"]
-    seqs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
-                      np.random.default_rng(3).choice(64, 14, replace=False).tolist()))
-    check(c, f"c5 sampled {len(seqs)} of 64 sequences", seqs=seqs)
+    say(f"[case] c5 S={c['num_seqs']} Hq={c['Hq']} Hkv={c['Hkv']} d={c['d']} tokens={int(c['seq_lens'].sum())}")
+    o, lse = run(c)
+    og, lg = host_f64(o), host_f64(lse)
+    parts = parallel_map(lambda s: oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"],
+                                                       c["seq_lens"], c["scale"], seqs=[s], dtype="bf16"),
+                         range(c["num_seqs"]), "c5")
+    o_ref = np.concatenate([p[0] for p in parts])
+    l_ref = np.concatenate([p[1] for p in parts])
+    compare(og, lg, o_ref, l_ref, BF16_TOL, "c5 all 64 sequences")
+
+
+def test_decode_lengths_past_max_seq_len_are_clamped():
+    """seq_lens entries above max_seq_len break the caller contract; the
+    kernels clamp them, so the result is that of the clamped lengths and
+    neither pass reads or writes outside the workspace (NaN guard bands)."""
+    lens = [100, 3000, 2050]
+    c = workloads.make_decode(len(lens), 8, 2, 128, seq_lens=lens, max_seq_len=3000, seed=29)
+    t = to_dev(c)
+    max_len = 2048
+    need = attn_paged_decode_workspace_size(len(lens), 8, 128, max_len)
+    guard = 4096
+    buf = torch.full(((need + 2 * guard) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = buf.view(torch.uint8)[guard:guard + need]
+    o, lse = attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], max_seq_len=max_len, scale=c["scale"],
+                               workspace=ws)
+    torch.cuda.synchronize()
+    raw = buf.view(torch.uint8)
+    assert torch.isnan(raw[:guard].view(torch.float32)).all(), "write before the workspace"
+    assert torch.isnan(raw[guard + need:].view(torch.float32)).all(), "write past the workspace"
+    clamped = np.minimum(c["seq_lens"], max_len)
+    o_ref, l_ref = oracle.paged_decode(c["q"], c["k_pages"], c["v_pages"], c["block_table"], clamped, c["scale"],
+                                       dtype="bf16")
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, BF16_TOL, "decode lengths clamped to max_seq_len")
+
+
+def test_caller_buffers_are_checked():
+    """Wrong out= / lse= / workspace arguments raise before any launch."""
+    c = workloads.make_decode(2, 8, 2, 128, seq_lens=[40, 70], seed=30)
+    t = to_dev(c)
+    kw = dict(max_seq_len=c["max_seq_len"], scale=c["scale"])
+    bad_out = [torch.empty((2, 8, 64), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((2, 8, 128), dtype=torch.float32, device="cuda"),
+               torch.empty((2, 8, 256), dtype=torch.bfloat16, device="cuda")[:, :, ::2],
+               torch.empty((2, 8, 128), dtype=torch.bfloat16)]
+    for out in bad_out:
+        with pytest.raises(ValueError):
+            attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], out=out, **kw)
+    for lse in [torch.empty((2, 7), dtype=torch.float32, device="cuda"),
+                torch.empty((2, 8), dtype=torch.bfloat16, device="cuda")]:
+        with pytest.raises(ValueError):
+            attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], lse=lse, **kw)
+    with pytest.raises(ValueError):
+        attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], workspace=torch.empty(1 << 20, dtype=torch.uint8),
+                          **kw)
+    # a too-small workspace is the library's own error
+    with pytest.raises(RuntimeError):
+        attn_paged_decode(t["q"], t["k"], t["v"], t["bt"], t["sl"],
+                          workspace=torch.empty(16, dtype=torch.uint8, device="cuda"), **kw)

@@ -9,7 +9,8 @@ import torch
 
 import workloads
 from exact_io_aware_fwd_amd import attn_fwd
-from _gpu_helpers import BF16_TOL, F32_TOL, compare, dev, doc_tensor, host_f64, oracle_prefill, say
+from _gpu_helpers import (BF16_TOL, F32_TOL, compare, dev, doc_tensor, host_f64, oracle_document_by_parts,
+                          oracle_prefill, oracle_prefill_by_head, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +115,53 @@ def test_lse_optional():
     assert torch.equal(o1, o2)
 
 
+def test_caller_buffers_are_checked():
+    """Wrong out= / lse= arguments raise before any launch: the library sees
+    only pointers and would write past a short buffer."""
+    case = workloads.make_prefill(1, 4, 2, 130, 130, 128, seed=14, mask="causal")
+    q, k, v = dev(case["q"], "bf16"), dev(case["k"], "bf16"), dev(case["v"], "bf16")
+    bad_out = [torch.empty((1, 4, 129, 128), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((1, 4, 130, 128), dtype=torch.float32, device="cuda"),
+               torch.empty((1, 4, 130, 256), dtype=torch.bfloat16, device="cuda")[..., ::2],
+               torch.empty((1, 4, 130, 128), dtype=torch.bfloat16)]
+    for out in bad_out:
+        with pytest.raises(ValueError):
+            attn_fwd(q, k, v, mask="causal", out=out)
+    for lse in [torch.empty((1, 4, 131), dtype=torch.float32, device="cuda"),
+                torch.empty((1, 4, 130), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((4, 130), dtype=torch.float32, device="cuda")]:
+        with pytest.raises(ValueError):
+            attn_fwd(q, k, v, mask="causal", lse=lse)
+
+
 # ------------------------------------------------------------ full-size configs
+#
+# Each configuration runs once on the GPU, with the arguments and launch
+# configuration the benchmark times, and every row of every head is compared
+# with the oracle.  The oracle runs one (batch, head) slice per host thread;
+# the document configuration runs through the per-document causal reduction
+# (rows of document [a, b) are causal attention over keys [a, b) alone),
+# plus a sample of rows through the full 32768-key rows.
+
+_GPU = {}
+
+
+def gpu_config(name):
+    """The kernel's output for a named configuration, computed once per module."""
+    if name not in _GPU:
+        case = workloads.prefill_config(name)
+        say(f"[case] {name} B={case['B']} Hq={case['Hq']} Hkv={case['Hkv']} N={case['Nq']} d={case['d']} "
+            f"mask={case['mask']} W={case['window']}")
+        q, k, v = dev(case["q"], case["dtype"]), dev(case["k"], case["dtype"]), dev(case["v"], case["dtype"])
+        o, lse = attn_fwd(q, k, v, scale=case["scale"], mask=case["mask"], window=case["window"],
+                          doc_offsets=doc_tensor(case))
+        torch.cuda.synchronize()
+        _GPU.clear()   # keep one configuration's inputs and outputs on the host at a time
+        _GPU[name] = (case, host_f64(o), host_f64(lse))
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return _GPU[name]
+
 
 def sample_rows(N, seed, extra=()):
     rng = np.random.default_rng(seed)
@@ -126,22 +173,31 @@ def sample_rows(N, seed, extra=()):
 
 @pytest.mark.slow
 def test_config_causal_b4h16n2048_all_rows():
-    case = workloads.prefill_config("c2_causal_b4h16n2048")
-    run_case(case, label="c2 all rows")
+    case, og, lg = gpu_config("c2_causal_b4h16n2048")
+    o_ref, l_ref = oracle_prefill_by_head(case, "c2")
+    compare(og, lg, o_ref, l_ref, BF16_TOL, "c2 all rows")
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["c3a_gqa_causal_n8192", "c3b_gqa_window1024_n8192"])
-def test_config_gqa_n8192_sampled_rows(name):
-    case = workloads.prefill_config(name)
-    rows = sample_rows(case["Nq"], 1, extra=range(1020, 1030))
-    run_case(case, rows=rows, label=f"{name} sampled {rows.size} rows/head")
+def test_config_gqa_n8192_all_rows(name):
+    case, og, lg = gpu_config(name)
+    o_ref, l_ref = oracle_prefill_by_head(case, name)
+    compare(og, lg, o_ref, l_ref, BF16_TOL, f"{name} all {case['Nq']} rows of {case['Hq']} heads")
 
 
 @pytest.mark.slow
-def test_config_document_n32768_sampled_rows():
-    case = workloads.prefill_config("c4_document_n32768")
+def test_config_document_n32768_all_rows_per_document():
+    case, og, lg = gpu_config("c4_document_n32768")
+    o_ref, l_ref = oracle_document_by_parts(case, "c4")
+    compare(og, lg, o_ref, l_ref, BF16_TOL, f"c4 all {case['Nq']} rows of {case['Hq']} heads (per document)")
+
+
+@pytest.mark.slow
+def test_config_document_n32768_sampled_full_rows():
+    case, og, lg = gpu_config("c4_document_n32768")
     off = case["doc_offsets"]
     edges = list(off[:-1]) + list(off[1:] - 1) + list(off[1:-1] - 1) + list(off[1:-1] + 1)
     rows = sample_rows(case["Nq"], 2, extra=edges)
-    run_case(case, rows=rows, label=f"c4 sampled {rows.size} rows/head")
+    o_ref, l_ref = oracle_prefill(case, rows=rows)
+    compare(og[:, :, rows], lg[:, :, rows], o_ref, l_ref, BF16_TOL, f"c4 sampled {rows.size} full rows/head")

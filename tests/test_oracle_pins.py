@@ -13,7 +13,10 @@ or index, a transposed operand, an off-by-one mask) fails at least one test:
   * the worked example printed on the "Attention Is the Bottleneck" page
     (section "FlashAttention: same math, different IO"): the running-max /
     running-sum form agrees with the full softmax to rounding noise;
-  * the split-KV log-sum-exp combine of the Flash-Decoding section.
+  * the split-KV log-sum-exp combine of the Flash-Decoding section;
+  * the bf16 helpers: widening of every one of the 65,536 bit patterns
+    against torch's own conversion and hand-decoded patterns, and rounding
+    to the nearest bf16 against torch's float32 rounding and exact ties.
 """
 import json
 import math
@@ -31,6 +34,94 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def rnd(seed, *shape):
     return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ------------------------------------------------------------ bf16 helpers
+
+def test_from_bf16_bits_every_pattern_matches_torch():
+    """All 65,536 bf16 bit patterns widen exactly as torch widens its bfloat16."""
+    import torch
+
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.from_bf16_bits(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)           # NaNs compared by class
+    assert nan.sum() == 2 * 127                          # exponent all ones, mantissa non-zero, both signs
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("pattern,value", [
+    (0x3F80, 1.0), (0xBF80, -1.0), (0xC000, -2.0), (0x3FC0, 1.5), (0x4049, 3.140625),
+    (0x0001, 2.0 ** -133),                               # smallest subnormal
+    (0x007F, 127 * 2.0 ** -133),                         # largest subnormal
+    (0x0080, 2.0 ** -126),                               # smallest normal
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),            # largest finite
+    (0x7F80, np.inf), (0xFF80, -np.inf), (0x0000, 0.0),
+])
+def test_from_bf16_bits_hand_decoded(pattern, value):
+    # sign | 8 exponent bits (bias 127) | 7 mantissa bits, decoded by hand above
+    got = oracle.from_bf16_bits(np.array([pattern], dtype=np.uint16))[0]
+    assert got == value
+
+
+def test_from_bf16_bits_negative_zero_and_shape():
+    got = oracle.from_bf16_bits(np.array([[0x8000, 0x3F80], [0x4000, 0x7FC1]], dtype=np.uint16))
+    assert got.shape == (2, 2) and got.dtype == np.float64
+    assert got[0, 0] == 0.0 and np.signbit(got[0, 0])
+    assert got[0, 1] == 1.0 and got[1, 0] == 2.0 and np.isnan(got[1, 1])
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    """On float32 inputs a single rounding is what torch's float -> bfloat16 does."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    f = (rng.standard_normal(400_000) * 10.0 ** rng.integers(-44, 38, 400_000)).astype(np.float32)
+    f = np.concatenate([f[np.isfinite(f)], np.float32([0.0, -0.0, 1e-45, -3e-39, 3.3e38])])
+    ours = oracle.round_to_bf16(f.astype(np.float64))
+    ref = torch.from_numpy(f).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_round_to_bf16_ties_and_near_ties():
+    """Ties go to the even significand; a near-tie that a double rounding
+    through float32 would turn into a tie still rounds to the nearer value."""
+    u = 2.0 ** -7                                        # spacing in [1, 2)
+    cases = [
+        (1.0 + u / 2, 1.0),                              # tie, 1.0 is even
+        (1.0 + 3 * u / 2, 1.0 + 2 * u),                  # tie, 1 + 2u is even
+        (1.0 + u / 2 + 2.0 ** -40, 1.0 + u),             # just above the tie (float32 would drop the 2^-40)
+        (1.0 + u / 2 - 2.0 ** -40, 1.0),
+        (-(2.0 + u), -2.0),                              # tie at spacing 2u, sign kept
+        (2.0 ** -134, 0.0),                              # subnormal tie between 0 and 2^-133
+        (3 * 2.0 ** -134, 2.0 ** -132),                  # subnormal tie, even side
+        (2.0 ** -134 + 2.0 ** -170, 2.0 ** -133),
+        ((2.0 - 2.0 ** -8) * 2.0 ** 127, np.inf),        # halfway to the next binade: overflows
+        ((2.0 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -50), (2.0 - 2.0 ** -7) * 2.0 ** 127),
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(oracle.round_to_bf16(x), want)
+    assert np.isnan(oracle.round_to_bf16(np.array([np.nan]))[0])
+
+
+def test_round_to_bf16_is_nearest_and_idempotent():
+    """Every result is a bf16 value, no other bf16 value is nearer, and bf16
+    values are fixed points."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.from_bf16_bits(bits)
+    fin = np.isfinite(vals)
+    assert np.array_equal(oracle.round_to_bf16(vals[fin]), vals[fin])
+    grid = np.unique(vals[fin])                          # every finite bf16 value, sorted
+    x = np.random.default_rng(6).standard_normal(200_000) * 10.0 ** np.random.default_rng(7).integers(-20, 20, 200_000)
+    r = oracle.round_to_bf16(x)
+    idx = np.searchsorted(grid, x)
+    lo, hi = grid[np.clip(idx - 1, 0, grid.size - 1)], grid[np.clip(idx, 0, grid.size - 1)]
+    best = np.minimum(np.abs(x - lo), np.abs(x - hi))
+    assert np.isin(r, grid).all()
+    assert np.array_equal(np.abs(x - r), best)
 
 
 # ---------------------------------------------------------------- brute force
