@@ -6,9 +6,10 @@
 //   P = exp(S - LSE),  D = rowsum(dO o O),  dS = P o (dO V^T - D)
 //   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q
 //
-// Three passes, no atomics on the gradients:
-//   prep   per query row: -LSE log2(e), D, the row's visible key interval,
-//          and the learned sink's gradient -sum_i P_sink,i D_i;
+// Three passes, no atomics:
+//   prep   per query row: -LSE log2(e), D and the row's visible key interval
+//          (then, with a learned sink, a per-head reduction of its gradient
+//          -sum_i P_sink,i D_i in a fixed order);
 //   dQ     one workgroup per (batch, query head, 128-row query tile), each
 //          wave owning 32 rows as in the forward; per 32-key tile it
 //          recomputes S^T = K Q^T and dP^T = V dO^T and accumulates
@@ -120,11 +121,6 @@ __device__ __forceinline__ PrefillParams mask_params(const BackwardParams& p) {
 
 }  // namespace
 
-__global__ void bwd_zero_kernel(float* x, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) x[i] = 0.f;
-}
-
 // D / 8 threads per query row (8 columns each): D = dO . O, plus the row's
 // statistics for the two gradient passes.  256 / (D / 8) rows per workgroup.
 template <int D>
@@ -145,7 +141,6 @@ __device__ __forceinline__ void bwd_prep_body(BackwardParams p) {
     for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
     if (rg < rows && t % TPR == 0) {
         const int i = (int)(rg % p.Nq);
-        const int h = (int)((rg / p.Nq) % p.Hq);
         const float L = p.lse[rg];
         p.ws_d[rg] = acc;
         p.ws_nl[rg] = L > -__builtin_inff() ? -L * kLog2e : 0.f;
@@ -154,9 +149,39 @@ __device__ __forceinline__ void bwd_prep_body(BackwardParams p) {
         row_interval(m, i, lo, hi);
         p.ws_lo[rg] = lo;
         p.ws_hi[rg] = hi;
-        if (p.dsink != nullptr && p.sink_logits != nullptr && L > -__builtin_inff())
-            atomicAdd(p.dsink + h, -__builtin_amdgcn_exp2f((p.sink_logits[h] - L) * kLog2e) * acc);
     }
+}
+
+// The learned sink's gradient, dsink[h] = -sum over (batch, row) of
+// P_sink D with P_sink = exp(sink[h] - LSE), from the saved LSE and the prep
+// pass's D.  One workgroup per query head; every thread sums its rows in a
+// fixed order and the workgroup adds the partial sums in a fixed tree, so the
+// result is the same bit for bit on every run (no atomics).
+__global__ __launch_bounds__(256) void bwd_dsink_kernel(BackwardParams p) {
+    __shared__ float part[256];
+    const int h = blockIdx.x, t = threadIdx.x;
+    const float s2 = p.sink_logits[h] * kLog2e;
+    float acc = 0.f;
+    for (int b = 0; b < p.B; ++b) {
+        const size_t base = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+        for (int i = t; i < p.Nq; i += 256) {
+            const float L = p.lse[base + i];
+            if (L > -__builtin_inff()) acc -= __builtin_amdgcn_exp2f(s2 - L * kLog2e) * p.ws_d[base + i];
+        }
+    }
+    part[t] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (t < w) part[t] += part[t + w];
+        __syncthreads();
+    }
+    if (t == 0) p.dsink[h] = part[0];
+}
+
+void launch_dsink(const BackwardParams& p, hipStream_t stream) {
+    if (p.dsink == nullptr || p.Hq == 0) return;
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(p.Hq), dim3(256), 0, stream, p);
 }
 
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) { bwd_prep_body<128>(p); }
@@ -614,10 +639,6 @@ int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
     p.ws_d = (float*)((char*)ws + stride);
     p.ws_lo = (int32_t*)((char*)ws + 2 * stride);
     p.ws_hi = (int32_t*)((char*)ws + 3 * stride);
-    // the sink gradient accumulates across rows: clear it with a kernel (not a
-    // memset, so the sequence can be captured into a graph)
-    if (p.dsink != nullptr && p.Hq > 0)
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3((p.Hq + 255) / 256), dim3(256), 0, stream, p.dsink, p.Hq);
     const dim3 wg(256), gq(p.B * p.Hq * p.num_q_tiles), gk(p.B * p.Hkv * p.num_k_tiles);
     if (rows > 0) {
         const size_t rows_per_wg = 256 / (d / 8);   // the prep pass's D / 8 threads per row
@@ -632,6 +653,7 @@ int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
             else hipLaunchKernelGGL(bwd_dq_d64_kernel, gq, wg, 0, stream, p);
         }
     }
+    launch_dsink(p, stream);   // after prep (it reads D); also with no rows, where it writes 0
     if ((long long)p.B * p.Hkv * p.num_k_tiles > 0) {
         if (d == 128) {
             if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, gk, wg, 0, stream, p);

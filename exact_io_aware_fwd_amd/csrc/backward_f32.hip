@@ -39,15 +39,10 @@ __device__ __forceinline__ float f32_logit(const BackwardParams& p, float x, flo
     return (x + slope * (float)dist) * kLog2e;
 }
 
-__global__ void f32_zero_kernel(float* x, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) x[i] = 0.f;
-}
-
 }  // namespace
 
-// One thread per query row: D = dO . O, -LSE log2 e, the row's key interval,
-// and the learned sink's gradient.
+// One thread per query row: D = dO . O, -LSE log2 e and the row's key
+// interval (the learned sink's gradient is reduced from D afterwards).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_f32_prep_kernel(BackwardParams p) {
     const long long rows = (long long)p.B * p.Hq * p.Nq;
@@ -58,7 +53,6 @@ __global__ __launch_bounds__(256) void bwd_f32_prep_kernel(BackwardParams p) {
     float acc = 0.f;
     for (int c = 0; c < D; ++c) acc = __builtin_fmaf(o[c], g[c], acc);
     const int i = (int)(rg % p.Nq);
-    const int h = (int)((rg / p.Nq) % p.Hq);
     const float L = p.lse[rg];
     p.ws_d[rg] = acc;
     p.ws_nl[rg] = L > -__builtin_inff() ? -L * kLog2e : 0.f;
@@ -66,8 +60,6 @@ __global__ __launch_bounds__(256) void bwd_f32_prep_kernel(BackwardParams p) {
     row_interval(f32_mask_params(p), i, lo, hi);
     p.ws_lo[rg] = lo;
     p.ws_hi[rg] = hi;
-    if (p.dsink != nullptr && p.sink_logits != nullptr && L > -__builtin_inff())
-        atomicAdd(p.dsink + h, -__builtin_amdgcn_exp2f((p.sink_logits[h] - L) * kLog2e) * acc);
 }
 
 // dQ: one wave per query row, over the row's visible keys.
@@ -181,8 +173,6 @@ int launch_backward_f32(BackwardParams p, int d, void* ws, hipStream_t stream) {
     p.ws_lo = (int32_t*)((char*)ws + 2 * stride);
     p.ws_hi = (int32_t*)((char*)ws + 3 * stride);
     const dim3 wg(256);
-    if (p.dsink != nullptr && p.Hq > 0)
-        hipLaunchKernelGGL(f32_zero_kernel, dim3((p.Hq + 255) / 256), wg, 0, stream, p.dsink, p.Hq);   // a kernel, not a memset: capturable
     if (rows > 0) {
         const dim3 gp((unsigned)((rows + 255) / 256)), gq((unsigned)((rows + 3) / 4));
         if (d == 128) {
@@ -193,6 +183,7 @@ int launch_backward_f32(BackwardParams p, int d, void* ws, hipStream_t stream) {
             hipLaunchKernelGGL(bwd_f32_dq_kernel<64>, gq, wg, 0, stream, p);
         }
     }
+    launch_dsink(p, stream);   // after prep (it reads D); also with no rows, where it writes 0
     if (keys > 0) {
         const dim3 gk((unsigned)((keys + 3) / 4));
         if (d == 128) hipLaunchKernelGGL(bwd_f32_dkdv_kernel<128>, gk, wg, 0, stream, p);

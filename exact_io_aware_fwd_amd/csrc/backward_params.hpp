@@ -40,5 +40,7 @@ struct BackwardParams {
 size_t backward_workspace_bytes(int B, int Hq, int Nq);
 int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream);   // d: 64 or 128
 int launch_backward_f32(BackwardParams p, int d, void* ws, hipStream_t stream);   // fp32 tensors, same workspace
+// dsink[h] from the saved LSE and the prep pass's D (no-op without a sink gradient)
+void launch_dsink(const BackwardParams& p, hipStream_t stream);
 
 }  // namespace xattn

@@ -59,6 +59,24 @@ def run_case(c, label, sink_tokens=0, sinks=None, softcap=0.0, slopes=None):
         check_grad(host_f64(ds), ref[3], f"{label} dsink")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_bitwise_identical_run_to_run(dtype):
+    """Every gradient, the sink's included, is the same bit for bit on every
+    call: no pass uses atomics (the sink gradient is a fixed-order reduction)."""
+    c = workloads.make_backward(2, 8, 2, 700, 700, 128, dtype=dtype, seed=75, mask="window", window=200)
+    q, k, v, do = (dev(c[x], dtype) for x in ("q", "k", "v", "do"))
+    sinks = torch.from_numpy(np.random.default_rng(76).normal(0.0, 1.5, 8).astype(np.float32)).cuda()
+    kw = dict(scale=c["scale"], mask="window", window=200, sink_tokens=4, sink_logits=sinks)
+    o, lse = attn_fwd(q, k, v, **kw)
+    first = attn_bwd(q, k, v, o, do, lse, **kw)
+    for _ in range(3):
+        again = attn_bwd(q, k, v, o, do, lse, **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "dsink"), first, again):
+            assert torch.equal(a, b), f"{dtype} {name} differs between calls"
+    say(f"[grad] {dtype}: four calls bit-identical, dsink {first[3].tolist()}")
+
+
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 100), ("document", 0)])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)])
 def test_backward_masks(mask, window, Hq, Hkv):
