@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     attn_bwd_workspace_size,
     attn_fwd,
     attn_paged_decode,
+    attn_paged_decode_noalloc,
     attn_paged_decode_workspace_size,
     attn_paged_prefill,
 )

@@ -170,6 +170,45 @@ def attn_paged_decode(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
     return out, lse
 
 
+def attn_paged_decode_noalloc(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
+                              scale: float | None = None, sink_logits: torch.Tensor | None = None,
+                              softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                              with_lse: bool = True, stream=None):
+    """attn_paged_decode without a workspace: the library's own device scratch
+    array holds the partials (calls that overlap on one GPU race).  Pass out=
+    and lse= to keep the call free of allocations."""
+    _need(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad shapes")
+    _need(q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16,
+          "paged decode is bf16")
+    _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k_pages, v_pages, block_table, seq_lens)),
+          "inputs must be contiguous device tensors")
+    S, Hq, d = q.shape
+    _, Hkv, page_size, _ = k_pages.shape
+    _need(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,), "index shapes")
+    _same_device(q.device, k_pages, v_pages, block_table, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buffer(lse, "lse", (S, Hq), torch.float32, q.device)
+    st = _lib.lib().attn_paged_decode_noalloc(ctypes_ptr(q), ctypes_ptr(k_pages), ctypes_ptr(v_pages),
+                                              ctypes_ptr(block_table), ctypes_ptr(seq_lens), ctypes_ptr(out),
+                                              None if lse is None else ctypes_ptr(lse),
+                                              S, Hq, Hkv, d, page_size, block_table.shape[1], int(max_seq_len),
+                                              float(scale), _sink_ptr(sink_logits, Hq), float(softcap),
+                                              _slopes_ptr(alibi_slopes, Hq), _stream(stream))
+    _lib.check(st)
+    return out, lse
+
+
 def attn_paged_prefill(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                        block_table: torch.Tensor, seq_lens: torch.Tensor, q_offsets: torch.Tensor, *,
                        max_seq_len: int, max_q_len: int, scale: float | None = None, mask: str = "causal",

@@ -107,13 +107,13 @@ extern "C" size_t attn_paged_decode_workspace_size(int num_seqs, int Hq, int d, 
     return xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len);
 }
 
-extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
-                                 const int32_t* block_table, const int32_t* seq_lens,
-                                 void* o, float* lse,
-                                 int num_seqs, int Hq, int Hkv, int d, int page_size,
-                                 int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
-                                 float softcap, const float* alibi_slopes,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Argument checks of a paged decode call, everything but the workspace.
+int decode_args_ok(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                   const int32_t* seq_lens, void* o, int num_seqs, int Hq, int Hkv, int d, int page_size,
+                   int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits, float softcap,
+                   const float* alibi_slopes) {
     if (num_seqs < 0 || Hq < 0 || Hkv < 0 || d < 0 || max_pages_per_seq < 0 || max_seq_len < 0)
         return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
@@ -131,12 +131,15 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
         return ATTN_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
         return ATTN_ERR_INVALID_ARGUMENT;
-    const size_t need = xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len);
-    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
     const long long splits = (max_seq_len + xattn::kSplitTokens - 1) / xattn::kSplitTokens;
     if ((long long)num_seqs * Hkv * (splits > 0 ? splits : 1) > kMaxGrid) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
 
+void decode_launch(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                   const int32_t* seq_lens, void* o, float* lse, int num_seqs, int Hq, int Hkv, int d,
+                   int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits, float softcap,
+                   const float* alibi_slopes, void* workspace, hipStream_t stream) {
     xattn::DecodeParams p;
     p.q = (const uint16_t*)q; p.kp = (const uint16_t*)k_pages; p.vp = (const uint16_t*)v_pages;
     p.block_table = block_table; p.seq_lens = seq_lens;
@@ -149,6 +152,45 @@ extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void*
     p.alibi_slopes = alibi_slopes;
     p.ws_o = nullptr; p.ws_lse = nullptr;
     xattn::launch_decode(p, d, max_seq_len, workspace, stream);
+}
+
+}  // namespace
+
+extern "C" int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 void* o, float* lse,
+                                 int num_seqs, int Hq, int Hkv, int d, int page_size,
+                                 int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
+                                 float softcap, const float* alibi_slopes,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int st = decode_args_ok(q, k_pages, v_pages, block_table, seq_lens, o, num_seqs, Hq, Hkv, d, page_size,
+                                  max_pages_per_seq, max_seq_len, scale, sink_logits, softcap, alibi_slopes);
+    if (st != ATTN_OK || (long long)num_seqs * Hq == 0) return st;
+    const size_t need = xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
+    decode_launch(q, k_pages, v_pages, block_table, seq_lens, o, lse, num_seqs, Hq, Hkv, d, max_pages_per_seq,
+                  max_seq_len, scale, sink_logits, softcap, alibi_slopes, workspace, stream);
+    return hip_status(hipGetLastError());
+}
+
+extern "C" int attn_paged_decode_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         void* o, float* lse,
+                                         int num_seqs, int Hq, int Hkv, int d, int page_size,
+                                         int max_pages_per_seq, int max_seq_len, float scale,
+                                         const float* sink_logits, float softcap, const float* alibi_slopes,
+                                         hipStream_t stream) {
+    const int st = decode_args_ok(q, k_pages, v_pages, block_table, seq_lens, o, num_seqs, Hq, Hkv, d, page_size,
+                                  max_pages_per_seq, max_seq_len, scale, sink_logits, softcap, alibi_slopes);
+    if (st != ATTN_OK || (long long)num_seqs * Hq == 0) return st;
+    if (xattn::decode_workspace_bytes(num_seqs, Hq, d, max_seq_len) > xattn::kNoAllocScratchBytes)
+        return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const hipError_t e = xattn::decode_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    decode_launch(q, k_pages, v_pages, block_table, seq_lens, o, lse, num_seqs, Hq, Hkv, d, max_pages_per_seq,
+                  max_seq_len, scale, sink_logits, softcap, alibi_slopes, ws, stream);
     return hip_status(hipGetLastError());
 }
 

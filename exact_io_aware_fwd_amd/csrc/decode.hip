@@ -35,6 +35,7 @@
 #include "common.hpp"
 #include "decode_params.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace xattn {
@@ -384,6 +385,36 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
         orow[lane] = (uint16_t)(w & 0xffffu);
     }
     if (p.lse != nullptr && lane == 0) p.lse[pair] = (mx + fast_log2(den)) * kLn2;
+}
+
+// Scratch of the allocation-free decode entry point: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// it takes each device's address once, with that device current, and uses
+// that address from then on.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len) {

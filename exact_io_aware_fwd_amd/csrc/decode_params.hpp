@@ -38,7 +38,14 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
     return len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
 }
 
+// Size of the device scratch array behind the allocation-free decode entry
+// point (the decode workspace of one call must fit in it).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+
 size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int max_seq_len);
+// This device's address of the scratch array (looked up once per device,
+// with that device current).
+hipError_t decode_scratch(void** ptr);
 int launch_decode(DecodeParams p, int d, int max_seq_len, void* ws, hipStream_t stream);
 
 }  // namespace xattn

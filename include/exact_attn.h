@@ -187,6 +187,32 @@ int attn_paged_decode(const void* q, const void* k_pages, const void* v_pages,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_paged_decode_noalloc — attn_paged_decode for callers that cannot
+ * allocate device memory or bring a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * result as attn_paged_decode (same kernels), minus the workspace: the
+ * partials go to a device array of ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing; its first call on a device looks up that device's
+ * array address once.
+ *
+ * Limit: attn_paged_decode_workspace_size(num_seqs, Hq, d, max_seq_len) must
+ * not exceed ATTN_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 64 sequences x 32
+ * query heads x 32K keys at d = 128 need 33.8 MB), else
+ * ATTN_ERR_WORKSPACE_TOO_SMALL and nothing runs.  Every call on one GPU uses
+ * the same array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The array needs no
+ * clearing between calls (each call writes every partial it reads).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_paged_decode_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* o, float* lse,
+                              int num_seqs, int Hq, int Hkv, int d, int page_size,
+                              int max_pages_per_seq, int max_seq_len, float scale, const float* sink_logits,
+                              float softcap, const float* alibi_slopes, hipStream_t stream);
+
+/*
  * attn_paged_prefill — chunked prefill over the paged KV cache: each
  * sequence appends a chunk of new tokens and those tokens attend to the
  * sequence's whole cache, read through its block table.  This is the serving

@@ -14,5 +14,6 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # Heavier GPU cases run after the small ones so a failure shows up early.
-    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+    # Heavier GPU cases run after the small ones so a failure shows up early;
+    # the allocation-free entry point's test (test_zz_*) runs last of all.
+    items.sort(key=lambda it: 2 if "test_zz_" in it.nodeid else (1 if it.get_closest_marker("slow") else 0))

@@ -19,9 +19,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_seven_entry_points():
+def test_header_declares_the_eight_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_paged_decode",
-                                    "attn_paged_decode_workspace_size", "attn_paged_prefill", "attn_status_string"]
+                                    "attn_paged_decode_noalloc", "attn_paged_decode_workspace_size",
+                                    "attn_paged_prefill", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -89,6 +90,33 @@ def test_decode_rejects_bad_arguments(kw, status):
 
 def test_decode_empty_is_noop():
     assert dec(q=None, o=None, S=0) == 0
+
+
+def dec_noalloc(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128, page=16,
+                max_pages=4, max_len=64, scale=0.1, sinks=None, softcap=0.0, alibi=None):
+    return _lib.lib().attn_paged_decode_noalloc(q, kp, vp, bt, sl, o, lse, S, Hq, Hkv, d, page, max_pages, max_len,
+                                                scale, sinks, softcap, alibi, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=32), 2), (dict(d=96), 2), (dict(Hq=6, Hkv=4), 1), (dict(max_pages=3), 1),
+    (dict(S=-1), 1), (dict(scale=0.0), 1), (dict(q=None), 1), (dict(sl=None), 1), (dict(bt=None), 1),
+    (dict(kp=FAKE + 2), 1), (dict(sinks=FAKE + 1), 1), (dict(softcap=-1.0), 1), (dict(alibi=FAKE + 2), 1),
+    # beyond the scratch array: 64 sequences x 32 heads x 64 1024-key splits x 129 floats > 64 MiB
+    (dict(S=64, Hq=32, Hkv=8, max_pages=4096, max_len=65536), 3),
+])
+def test_decode_noalloc_rejects_bad_arguments_before_any_hip_call(kw, status):
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_is_the_header_constant():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m is not None
+    limit = int(m.group(1)) << int(m.group(2))
+    f = xa.attn_paged_decode_workspace_size
+    assert f(64, 32, 128, 32768) <= limit < f(64, 32, 128, 65536)    # the decode workload fits, twice its length not
+    assert dec_noalloc(q=None, o=None, S=0) == 0
 
 
 def test_workspace_size():
