@@ -399,6 +399,8 @@ def main() -> int:
                     help="short run for counter collection: one known-size copy, then PMC_PLAN's launches")
     ap.add_argument("--repeat", type=int, default=1, help="--pmc-pass: run the plan's calls this many times over")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="every counter of one or more --pmc runs of --pmc-pass, per workload: profiles/sq_counters.json")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="per-workload kernel durations from a --kernel-trace run of --pmc-pass")
     ap.add_argument("--summarize-clock", metavar="DIR")
@@ -410,6 +412,8 @@ def main() -> int:
         return summarize_clock(args.summarize_clock)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
                                    "this build (--gpus must be 1)"}))
@@ -648,6 +652,47 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
                                      "fetch_bytes": float(np.mean(fv)) * 1024 * f_factor,
                                      "write_bytes": float(np.mean(wv)) * 1024 * w_factor}
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def summarize_counters(dirs: list) -> int:
+    """Mean per dispatch of every counter found in the --pmc runs (one
+    counter set per run), by workload and kernel, plus two derived ratios
+    for the attention kernels: VALU instructions per MFMA instruction, and
+    the fraction of MFMA-busy cycles in which VALU work issued beside it."""
+    import csv
+
+    names = set()
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                names.add(row["Counter_Name"])
+    out = {"source_sha256": source_digest(), "plan": PMC_PLAN, "runs": len(dirs),
+           "command": "rocprofv3 --pmc <up to 8 SQ counters> -f csv -d <dir> -o run -- python3 bench.py --pmc-pass "
+                      "(one run per counter set) ; python3 bench.py --summarize-counters <dir> ...",
+           "legs": {}}
+    for name in sorted(names):
+        vals: dict = {}
+        for d in dirs:
+            try:
+                vals.update(_read_counters(d, name))
+            except SystemExit:
+                pass
+        if not vals:
+            continue
+        for leg, per in _by_leg(vals).items():
+            for tag, v in per.items():
+                out["legs"].setdefault(leg, {}).setdefault(tag, {})[name] = float(np.mean(v))
+    for leg, per in out["legs"].items():
+        for tag, c in per.items():
+            if c.get("SQ_INSTS_MFMA"):
+                if "SQ_INSTS_VALU" in c:
+                    c["valu_per_mfma"] = round(c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"], 3)
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                c["coexec_per_mfma_busy"] = round(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+    path = os.path.join(ROOT, "profiles", "sq_counters.json")
+    json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out, indent=1))
     return 0
 

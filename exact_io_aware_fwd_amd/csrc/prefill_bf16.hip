@@ -38,6 +38,15 @@ struct PrefillBf16State {
     float m_run;
     float l_run;   // this lane's half of the row sum of the bf16 weights: normalises O
     float l_f32;   // same sum over the unrounded fp32 weights: gives the LSE
+    // the whole row's sum of the bf16 weights (every lane of the row pair)
+    __device__ __forceinline__ float l_total() const { return l_run + __shfl_xor(l_run, 32); }
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+        m_run = -__builtin_inff();
+        l_run = 0.f;
+        l_f32 = 0.f;
+    }
 };
 
 // Order one product's LDS operand reads against its MFMAs: the first
@@ -132,16 +141,11 @@ struct SwizzledTiles {
     static constexpr int kVHalf = 8 * 256;
 };
 
-// S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
-// key tile resident in LDS, laid out as T says.  MODS: the scores first go
-// through the score modifications sm (qpos: this lane's query position).
-template <int D, bool MODS = false, class T>
-__device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, int n0,
-                                          bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane,
-                                          const ScoreMod& sm = ScoreMod{}, int qpos = 0) {
+// S^T = K Q^T for one 64-key tile resident in LDS (laid out as T says): two
+// 32-key blocks, 16 MFMAs.
+template <int D, class T>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const PrefillBf16State<D>& st, const T& tl) {
     using C = PrefillBf16Cfg<D>;
-    // ---- S^T = K Q^T, two 32-key blocks
-    f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) s[jb] = f32x16{};
 #pragma unroll
@@ -151,7 +155,16 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
             const u32x4 a = *(const u32x4*)tl.k_at(jb, kk);
             s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), st.qf[kk], s[jb], 0, 0, 0);
         }
-    order_reads_ahead<2 * C::DK, 1, 4>();
+}
+
+// Score modifications, mask and the row max of a score tile, with the
+// conditional rescale; returns the reference the weights are taken against.
+// MODS: the raw q.k scores become base-2 logits here and scale_log2 becomes 1.
+template <int D, bool MODS>
+__device__ __forceinline__ float prepare_tile(PrefillBf16State<D>& st, f32x16 (&s)[2], int n0, bool full, int lo_i,
+                                              int hi_i, int sink_end, float& scale_log2, int lane, const ScoreMod& sm,
+                                              int qpos) {
+    using C = PrefillBf16Cfg<D>;
     // ---- score modifications: raw q.k -> base-2 logit (unit scale below).
     // Score 16 jb + r of this lane is key n0 + 4 (lane / 32) + 32 jb +
     // 8 (r / 4) + r % 4 (see the mask below).  They come before the mask, so
@@ -226,18 +239,24 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
         st.l_f32 *= alpha;
         st.m_run = m_new;
     }
-    const float m_use = st.m_run == neg_inf() ? 0.f : st.m_run;
-    // Weights, P^T operands and O^T += V^T P^T, one 16-key block kb at a time.
-    // O is normalised by the sum of the same bf16-rounded weights the PV
-    // product uses, so it is an exact weighted average of V rows under those
-    // weights (a dot with (1, 1) adds two packed bf16 values at once); the LSE
-    // uses the fp32 sum, free of the weights' rounding.
-    //
-    // The V^T operand comes from the row-major V tile through two transposing
-    // reads (ds_read_b64_tr_b16): in each 16-lane group, source lane 4k+q
-    // points at 4 columns c0+4q.. of key row k, and lane i receives column
-    // c0+i of those 4 rows.  Rows are picked so the 8 keys a lane holds are the
-    // ones its P^T operand slots hold.
+    return st.m_run == neg_inf() ? 0.f : st.m_run;
+}
+
+// Weights, P^T operands and O^T += V^T P^T, one 16-key block kb at a time.
+// O is normalised by the sum of the same bf16-rounded weights the PV
+// product uses, so it is an exact weighted average of V rows under those
+// weights (a dot with (1, 1) adds two packed bf16 values at once); the LSE
+// uses the fp32 sum, free of the weights' rounding.
+//
+// The V^T operand comes from the row-major V tile through two transposing
+// reads (ds_read_b64_tr_b16): in each 16-lane group, source lane 4k+q
+// points at 4 columns c0+4q.. of key row k, and lane i receives column
+// c0+i of those 4 rows.  Rows are picked so the 8 keys a lane holds are the
+// ones its P^T operand slots hold.
+template <int D, class T>
+__device__ __forceinline__ void softmax_pv(PrefillBf16State<D>& st, f32x16 (&s)[2], const T& tl, float scale_log2,
+                                           float m_use) {
+    using C = PrefillBf16Cfg<D>;
     float fs[4] = {0.f, 0.f, 0.f, 0.f};
     float ps[2] = {0.f, 0.f};
 #pragma unroll
@@ -267,6 +286,21 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
     }
     st.l_run += ps[0] + ps[1];
     st.l_f32 += (fs[0] + fs[1]) + (fs[2] + fs[3]);
+}
+
+// S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
+// key tile resident in LDS, laid out as T says.  MODS: the scores first go
+// through the score modifications sm (qpos: this lane's query position).
+template <int D, bool MODS = false, class T>
+__device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, int n0,
+                                          bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane,
+                                          const ScoreMod& sm = ScoreMod{}, int qpos = 0) {
+    using C = PrefillBf16Cfg<D>;
+    f32x16 s[2];
+    qk_tile<D>(s, st, tl);
+    order_reads_ahead<2 * C::DK, 1, 4>();
+    const float m_use = prepare_tile<D, MODS>(st, s, n0, full, lo_i, hi_i, sink_end, scale_log2, lane, sm, qpos);
+    softmax_pv<D>(st, s, tl, scale_log2, m_use);
     interleave_weights_products<4 * C::CB, 40, 6>();
 }
 
@@ -335,11 +369,7 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
                 st.qf[kk] = __builtin_bit_cast(bf16x8, w);
             }
         }
-    #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
-        st.m_run = neg_inf();   // running row max, base-2 scaled units
-        st.l_run = 0.f;
-        st.l_f32 = 0.f;
+        st.init();   // running row max -inf (base-2 scaled units), sums and O 0
 
         const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
@@ -392,7 +422,7 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
         const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
 
         // ---- epilogue: O = acc / l once, LSE in natural log (with the sink, if any)
-        const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+        const float l_tot = st.l_total();
         if (row_ok) {
             const float s2 = p.sink_logits != nullptr ? p.sink_logits[hq] * kLog2e : neg_inf();
             float inv, lse_row;
@@ -561,11 +591,7 @@ __device__ __forceinline__ void paged_prefill_bf16_body(PagedPrefillParams pp) {
             st.qf[kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
-    st.m_run = neg_inf();
-    st.l_run = 0.f;
-    st.l_f32 = 0.f;
+    st.init();
 
     const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
@@ -632,7 +658,7 @@ __device__ __forceinline__ void paged_prefill_bf16_body(PagedPrefillParams pp) {
         }
     }
     const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    const float l_tot = st.l_total();
     if (row_ok) {
         const float s2 = pp.sink_logits != nullptr ? pp.sink_logits[hq] * kLog2e : neg_inf();
         float inv, lse_row;
@@ -731,11 +757,7 @@ __device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
             st.qf[kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) st.acc[cb] = f32x16{};
-    st.m_run = neg_inf();
-    st.l_run = 0.f;
-    st.l_f32 = 0.f;
+    st.init();
 
     const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
@@ -807,7 +829,7 @@ __device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
         }
     }
     const float lf_tot = st.l_f32 + __shfl_xor(st.l_f32, 32);
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    const float l_tot = st.l_total();
     if (row_ok) {
         const float s2 = pp.sink_logits != nullptr ? pp.sink_logits[hq] * kLog2e : neg_inf();
         float inv, lse_row;
