@@ -308,15 +308,40 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
 // without it the tile loop and the mask compile to the one-interval form.
 // MODS: the score modifications are on (a kernel of its own, so the plain
 // kernel's code does not change).
+// Issue this wave's copies of one 64-key tile in the SwizzledTiles layout
+// (d = 128) from K or V rows that follow each other in memory: copy jj fills
+// tile rows 16 jj + 4 wave .. + 3, and lane l brings the source chunk that
+// lands swizzled at 16-byte slot l % 16 of row 4 wave + l / 16 (`lane_off`,
+// the same for every tile; jj only moves the source by 16 rows).  The buffer
+// resource starts at key n0 and covers the keys that exist, so rows past Nk
+// read as zeros.
+__device__ __forceinline__ void load_swz_tile_async(const uint16_t* __restrict__ base, int n0, int Nk, uint8_t* lds,
+                                                    uint32_t lane_off, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int D = 128;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (size_t)n0 * D), (short)0, (int)tile_range_bytes<D>(Nk - n0, 64), 0x00020000);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (4 * jj + wave) * 1024), 16, lane_off,
+                                                 jj * 16 * D * 2, 0, 0);
+#endif
+}
+
 template <int D, bool SINKS, bool MODS>
 __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
     using C = PrefillBf16Cfg<D>;
+    // Head dim 128 keeps its K/V tiles unpadded and swizzled (16 KiB each,
+    // 4 + 4 copies per wave and tile); head dim 64 keeps the padded tiles.
+    constexpr bool SWZ = D == 128;
+    constexpr int KT = SWZ ? C::BN * D * 2 : C::KTILE;
+    constexpr int VT = SWZ ? C::BN * D * 2 : C::VTILE;
     const int sink_end = SINKS ? p.sink_end : 0;
     // two stages of the K/V ring, as separate arrays so each access names its buffer
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::VTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[VT];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[VT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, lets loads use scalar control
@@ -374,11 +399,28 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
         const TileRange tr = tile_range(lo_wg, hi_wg, sink_end, C::BN);
 
         uint32_t koff[C::KLW], voff[C::VLW];
-        tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
-        tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
-        // this lane's operand bases inside a K / V tile
+        if constexpr (!SWZ) {
+            tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+            tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
+        }
+        // this lane's operand bases inside a K / V tile (padded layout)
         const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
         const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+        // swizzled layout: this lane's copy source offsets and operand offsets
+        const int rip = 4 * wave + (lane >> 4);
+        [[maybe_unused]] const uint32_t kso = (uint32_t)(rip * 256 + (((lane & 15) ^ rip) * 16));
+        [[maybe_unused]] const uint32_t vso = (uint32_t)(rip * 256 + (((lane & 15) ^ (4 * ((lane >> 4) & 3))) * 16));
+        SwizzledTiles stl;
+        if constexpr (SWZ) stl.init(lane);
+        auto copy_tile = [&](int t, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+            if constexpr (SWZ) {
+                load_swz_tile_async(kg_, t * C::BN, p.Nk, kd, kso, wave);
+                load_swz_tile_async(vg_, t * C::BN, p.Nk, vd, vso, wave);
+            } else {
+                load_tile_async<D, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kd, koff, wave);
+                load_tile_async<D, C::VS, C::VLOADS>(vg_, t * C::BN, p.Nk, vd, voff, wave);
+            }
+        };
 
         // One stage of the ring: wait for this tile's copies, make them visible to
         // every wave (which also proves every wave is done with the other stage),
@@ -395,24 +437,27 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
             // turn, tile by tile, evens them out: C2 181 K -> 174 K cycles.
             if (((it + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
-            if (it + 1 < tr.n) {
-                const int tn = tile_of(tr, it + 1);
-                load_tile_async<D, C::KS, C::KLOADS>(kg_, tn * C::BN, p.Nk, kn, koff, wave);
-                load_tile_async<D, C::VS, C::VLOADS>(vg_, tn * C::BN, p.Nk, vn, voff, wave);
-            }
+            // (issuing these copies one or two at a time between the S^T
+            // products, or after them, was 3-6 % slower than this burst)
+            if (it + 1 < tr.n) copy_tile(tile_of(tr, it + 1), kn, vn);
             const int n0 = tile_of(tr, it) * C::BN;
             const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < sink_end);
             if (active) {
                 const bool full = n0 + C::BN - 1 <= hi_w_first && (n0 >= lo_w_last || n0 + C::BN - 1 < sink_end);
-                tile_step<D, MODS>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end,
-                                   p.scale_log2, lane, sm, row + p.Nk - p.Nq);
+                if constexpr (SWZ) {
+                    stl.k = kc;
+                    stl.v = vc;
+                    tile_step<D, MODS>(st, stl, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane, sm,
+                                       row + p.Nk - p.Nq);
+                } else {
+                    tile_step<D, MODS>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end,
+                                       p.scale_log2, lane, sm, row + p.Nk - p.Nq);
+                }
             }
         };
 
         if (tr.n > 0) {
-            const int t0 = tile_of(tr, 0);
-            load_tile_async<D, C::KS, C::KLOADS>(kg_, t0 * C::BN, p.Nk, k_lds0, koff, wave);
-            load_tile_async<D, C::VS, C::VLOADS>(vg_, t0 * C::BN, p.Nk, v_lds0, voff, wave);
+            copy_tile(tile_of(tr, 0), k_lds0, v_lds0);
             for (int it = 0; it < tr.n; it += 2) {
                 stage(it, k_lds0, v_lds0, k_lds1, v_lds1);
                 if (it + 1 < tr.n) stage(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
