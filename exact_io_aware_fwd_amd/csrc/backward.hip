@@ -54,6 +54,60 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tl, int kb, int cb) 
     return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
+// One LDS copy of a d = 128 tile that serves both row reads and transposing
+// reads: 16-byte chunk c of row r is stored at chunk c ^ (4 (r % 4) + (r / 4) % 4).
+// 16 consecutive rows at one chunk (a row operand) land in 16 different
+// chunks, and the 4 consecutive rows x 64 bytes of a transposing read land in
+// 16 different chunks, so neither read has bank conflicts (checked on a CPU
+// model of the banks).  Each 1 KiB copy holds 4 whole rows, and a lane's
+// source offset is the same for all of a wave's copies.  Per-lane offsets:
+// ro[kk] for the row operand at head-dim step kk (32-row block jb adds 8 KiB),
+// tr0/tr1[cb] for the two transposing reads of column block cb (16-row block
+// kb adds 4 KiB), cpo for this wave's copies (block wave + 4 j, j KiB apart).
+struct DualSwizzle {
+    int ro[8], tr0[4], tr1[4];
+    uint32_t cpo;
+    __device__ __forceinline__ void init(int lane, int wave) {
+        const int gl = 4 * (lane & 3) + ((lane >> 2) & 3);   // the chunk swizzle of this lane's rows
+        const int y = (lane >> 5) ^ gl;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) ro[kk] = (lane & 31) * 256 + 32 * (kk ^ (y >> 1)) + 16 * (y & 1);
+        const int a = lane >> 5, bq = (lane >> 2) & 3, e = (lane >> 4) & 1, d = (lane & 3) >> 1;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            tr0[cb] = (4 * a + bq) * 256 + 64 * (cb ^ bq) + 16 * (2 * e + (d ^ a)) + 8 * (lane & 1);
+            tr1[cb] = (4 * a + bq + 8) * 256 + 64 * (cb ^ bq) + 16 * (2 * (e ^ 1) + (d ^ a)) + 8 * (lane & 1);
+        }
+        const int q = lane >> 4;
+        cpo = (uint32_t)(q * 256 + (((lane & 15) ^ (4 * q) ^ wave) * 16));
+    }
+    // A operand by rows: rows (lane & 31) + 32 jb, head-dim chunk 2 kk + (lane >> 5)
+    __device__ __forceinline__ bf16x8 row(const uint8_t* tile, int jb, int kk) const {
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + jb * 8192 + ro[kk]));
+    }
+    // A operand transposed, as tr_operand
+    __device__ __forceinline__ bf16x8 tr(const uint8_t* tile, int kb, int cb) const {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kb * 4096 + tr0[cb]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kb * 4096 + tr1[cb]));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    }
+    // this wave's copies of one tile of NB KiB (4 rows each) from rows
+    // following each other in memory; rows at or past `rows` read as zero
+    template <int NB>
+    __device__ __forceinline__ void copy(const uint16_t* src, int rows, uint8_t* lds, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)src, (short)0, (int)tile_range_bytes<128>(rows, NB * 4), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < NB / 4; ++j) {
+            const int blk = wave + 4 * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 1024), 16, cpo, blk * 1024, 0, 0);
+        }
+#endif
+    }
+};
+
 // Order a product's LDS operand reads AHEAD MFMAs ahead of their use (R
 // reads per MFMA), as the forward's tile step does.
 template <int NMFMA, int R, int AHEAD>
@@ -190,11 +244,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) { bwd_p
 __global__ __launch_bounds__(256) void bwd_prep_d64_kernel(BackwardParams p) { bwd_prep_body<64>(p); }
 
 // dQ: per 32-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
-// dQ^T += K^T dS^T.  K is copied twice (row and transposed layouts), V once.
-// With 32-key tiles a stage of that ring is 28 KiB and a wave needs 190
-// registers, so two workgroups share a CU and two waves each SIMD (64-key
-// tiles took 54 KiB per stage and 280 registers, one wave per SIMD; the
-// backward of C2 went from 468 to 414 us with this change).
+// dQ^T += K^T dS^T.  At d = 128 the K tile is one DualSwizzle copy that
+// serves the row reads (S^T) and the transposing reads (dQ^T), and V is
+// copied in the same layout: 16 KiB per stage, 4 copies per wave and tile.
+// At d = 64 K is copied twice (row and transposed padded layouts), V once.
+// With 32-key tiles a wave needs about 200 registers, so two workgroups share
+// a CU and two waves each SIMD (64-key tiles took 280 registers, one wave per
+// SIMD; the backward of C2 went from 468 to 414 us with 32-key tiles).
 template <int D>
 struct DqCfg {
     static constexpr int BN = 32;
@@ -219,12 +275,17 @@ template <int D, bool MODS>
 __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     using C = DqCfg<D>;
     constexpr int BM = 128;
-    __shared__ __attribute__((aligned(1024))) uint8_t kr0[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::VTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t vr0[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t kr1[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::VTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t vr1[C::KTILE];
+    constexpr bool SWZ = D == 128;
+    constexpr int RT = SWZ ? C::BN * D * 2 : C::KTILE;   // row-layout tile (K and V; the only tiles with SWZ)
+    constexpr int TT = SWZ ? 16 : C::VTILE;              // transposed-layout K tile (unused with SWZ)
+    __shared__ __attribute__((aligned(1024))) uint8_t kr0[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t kt0_[TT];
+    __shared__ __attribute__((aligned(1024))) uint8_t vr0[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t kr1[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t kt1_[TT];
+    __shared__ __attribute__((aligned(1024))) uint8_t vr1[RT];
+    uint8_t* kt0 = SWZ ? kr0 : kt0_;
+    uint8_t* kt1 = SWZ ? kr1 : kt1_;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -263,15 +324,28 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     const uint16_t* vg_ = p.v + ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk * D;
     const TileRange tr = tile_range(lo_wg, hi_wg, p.sink_end, C::BN);
     uint32_t koff[C::KLW], voff[C::VLW];
-    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
-    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
-    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
-    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+    int kbase = 0, vbase = 0;
+    DualSwizzle dz;
+    if constexpr (SWZ) {
+        dz.init(lane, wave);
+    } else {
+        tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+        tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
+        kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+        vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+    }
 
     auto copy = [&](int t, uint8_t* kr, uint8_t* kt, uint8_t* vr) __attribute__((always_inline)) {
-        load_tile_async<D, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kr, koff, wave);
-        load_tile_async<D, C::VS, C::VLOADS>(kg_, t * C::BN, p.Nk, kt, voff, wave);
-        load_tile_async<D, C::KS, C::KLOADS>(vg_, t * C::BN, p.Nk, vr, koff, wave);
+        if constexpr (SWZ) {
+            // keys past Nk read as zero
+            dz.template copy<C::BN / 4>(kg_ + (size_t)t * C::BN * D, p.Nk - t * C::BN, kr, wave);
+            dz.template copy<C::BN / 4>(vg_ + (size_t)t * C::BN * D, p.Nk - t * C::BN, vr, wave);
+            (void)kt;
+        } else {
+            load_tile_async<D, C::KS, C::KLOADS>(kg_, t * C::BN, p.Nk, kr, koff, wave);
+            load_tile_async<D, C::VS, C::VLOADS>(kg_, t * C::BN, p.Nk, kt, voff, wave);
+            load_tile_async<D, C::KS, C::KLOADS>(vg_, t * C::BN, p.Nk, vr, koff, wave);
+        }
     };
     auto stage = [&](int it, const uint8_t* kr, const uint8_t* kt, const uint8_t* vr, uint8_t* krn, uint8_t* ktn,
                      uint8_t* vrn) __attribute__((always_inline)) {
@@ -286,12 +360,14 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
         f32x16 s = f32x16{}, dp = f32x16{};
         const uint8_t* krl = kr + kbase;
         const uint8_t* vrl = vr + kbase;
+        auto rowop = [&](const uint8_t* tile, const uint8_t* tl, int kk) __attribute__((always_inline)) {
+            if constexpr (SWZ) return dz.row(tile, 0, kk);
+            else return __builtin_bit_cast(bf16x8, *(const u32x4*)(tl + kk * 32));
+        };
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, *(const u32x4*)(krl + kk * 32)), qf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, *(const u32x4*)(vrl + kk * 32)), df[kk], dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop(kr, krl, kk), qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop(vr, vrl, kk), df[kk], dp, 0, 0, 0);
         }
         order_operand_reads<D / 8, 1, 4>();
 #pragma unroll
@@ -329,12 +405,17 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
-                const uint8_t* vp = ktl + kb * 16 * C::VS * 16 + cb * 64;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), dsf[kb], acc[cb], 0, 0, 0);
+                bf16x8 a;
+                if constexpr (SWZ) {
+                    a = dz.tr(kt, kb, cb);
+                } else {
+                    const uint8_t* vp = ktl + kb * 16 * C::VS * 16 + cb * 64;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VS * 16));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                    a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+                }
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kb], acc[cb], 0, 0, 0);
             }
         order_operand_reads<D / 16, 2, 2>();
     };
@@ -452,24 +533,9 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
 
     uint32_t koff[C::KLW], voff[C::VLW];
     int kbase = 0, vbase = 0;
-    // SWZ: per-lane offsets of the row operand (head-dim step kk, 32-row block
-    // jb adds 8192), of the two transposing reads (column block cb), and of
-    // this wave's copies (block b = wave + 4 j adds b KiB)
-    int ro[8], tr0[4], tr1[4];
-    [[maybe_unused]] uint32_t cpo = 0;
+    DualSwizzle dz;
     if constexpr (SWZ) {
-        const int gl = 4 * (lane & 3) + ((lane >> 2) & 3);   // the chunk swizzle of this lane's rows
-        const int y = (lane >> 5) ^ gl;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) ro[kk] = (lane & 31) * 256 + 32 * (kk ^ (y >> 1)) + 16 * (y & 1);
-        const int a = lane >> 5, bq = (lane >> 2) & 3, e = (lane >> 4) & 1, d = (lane & 3) >> 1;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            tr0[cb] = (4 * a + bq) * 256 + 64 * (cb ^ bq) + 16 * (2 * e + (d ^ a)) + 8 * (lane & 1);
-            tr1[cb] = (4 * a + bq + 8) * 256 + 64 * (cb ^ bq) + 16 * (2 * (e ^ 1) + (d ^ a)) + 8 * (lane & 1);
-        }
-        const int q = lane >> 4;
-        cpo = (uint32_t)(q * 256 + (((lane & 15) ^ (4 * q) ^ wave) * 16));
+        dz.init(lane, wave);
     } else {
         tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
         tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
@@ -479,18 +545,12 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     // A operands: rows of a Q or dO tile (32-row block jb, head-dim step kk),
     // and a Q or dO tile transposed (16-row block kb, 32-column block cb)
     auto rowop = [&](const uint8_t* tile, int jb, int kk) __attribute__((always_inline)) {
-        if constexpr (SWZ) return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + jb * 8192 + ro[kk]));
+        if constexpr (SWZ) return dz.row(tile, jb, kk);
         else return row_operand<D>(tile + kbase, jb, kk);
     };
     auto trop = [&](const uint8_t* tile, int kb, int cb) __attribute__((always_inline)) {
-        if constexpr (SWZ) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kb * 4096 + tr0[cb]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kb * 4096 + tr1[cb]));
-            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-            return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-        } else {
-            return tr_operand<D>(tile + vbase, kb, cb);
-        }
+        if constexpr (SWZ) return dz.tr(tile, kb, cb);
+        else return tr_operand<D>(tile + vbase, kb, cb);
     };
 
     auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * p.group + it / ntq; };
@@ -503,20 +563,9 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         const uint16_t* qg = p.q + head_row * D;
         const uint16_t* dg = p.dO + head_row * D;
         if constexpr (SWZ) {
-#if defined(__HIP_DEVICE_COMPILE__)
-            // rows past Nq read as zero: the range covers the tile's rows that exist
-            const int range = (int)tile_range_bytes<D>(p.Nq - q0, BQ);
-            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qg + (size_t)q0 * D), (short)0,
-                                                                                range, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dg + (size_t)q0 * D), (short)0,
-                                                                                range, 0x00020000);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int blk = wave + 4 * j;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qr + blk * 1024), 16, cpo, blk * 1024, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dr + blk * 1024), 16, cpo, blk * 1024, 0, 0);
-            }
-#endif
+            // rows past Nq read as zero
+            dz.template copy<BQ / 4>(qg + (size_t)q0 * D, p.Nq - q0, qr, wave);
+            dz.template copy<BQ / 4>(dg + (size_t)q0 * D, p.Nq - q0, dr, wave);
             (void)qt;
             (void)dt;
         } else {
