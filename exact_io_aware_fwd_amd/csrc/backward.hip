@@ -19,10 +19,10 @@
 //          head of the group, recomputes S = Q K^T and dP = dO V^T with the
 //          keys as the accumulator columns, and accumulates dV^T += dO^T P
 //          and dK^T += Q^T dS.
-// Tiles that one product reads by rows and another transposed are copied to
-// LDS twice, once in each padded layout, so every read is conflict-free; the
-// dK/dV pass at d = 128 instead keeps one swizzled copy of each Q and dO tile
-// that both reads use without conflicts.
+// At d = 128 a tile that one product reads by rows and another transposed
+// (Q and dO in the dK/dV pass, K in the dQ pass) is one swizzled copy that
+// both reads use without bank conflicts (DualSwizzle); at d = 64 such tiles
+// are copied twice, once in each padded layout.
 #include "backward_params.hpp"
 #include "prefill_tiles.hpp"
 
