@@ -415,8 +415,8 @@ def main() -> int:
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
-                                   "this build (--gpus must be 1)"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the library has no multi-GPU path "
+                                   "(--gpus must be 1)"}))
         return 2
 
     import torch

@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, bad mask field ... */
-    ATTN_ERR_UNSUPPORTED = 2,         /* valid request this build does not implement (e.g. d) */
+    ATTN_ERR_UNSUPPORTED = 2,         /* valid request the library does not implement (e.g. d) */
     ATTN_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below attn_paged_decode_workspace_size */
     ATTN_ERR_HIP = 4                  /* a HIP launch failed; see attn_status_string */
 } attn_status;
