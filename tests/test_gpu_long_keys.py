@@ -1,0 +1,86 @@
+"""Sequences of more than 2^24 keys (d = 128).
+
+A K/V tile's buffer range is the tile's own rows that exist, rows * d * 2
+bytes with rows clamped to the tile.  Unclamped, Nk - n0 rows of 256 bytes
+wrap 32 bits once Nk - n0 passes 2^24, and the first tile of a sequence of
+2^24 + 40 keys would read its rows 40..63 as zeros.
+
+The checks use the closed form the oracle is pinned to for identical keys
+(tests/test_oracle_pins.py): with every key zero all scores are equal, so a
+row's output is the mean of V over the keys it sees and its LSE is
+ln(number of those keys), at any size.  V is zero except a few marked rows
+(the first tile's rows 40..63, rows past 2^23 and 2^24, the last rows), each
+in a column of its own, so every output column is a count of marked rows the
+row sees divided by its key count: a tile read as zeros, or from the wrong
+rows, zeroes or moves a column.  These outputs are about 1e-6, so they are
+compared relatively: bf16 rounding of the output (2^-9) plus the fp32 sums
+(1e-6), bound 2^-8."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_fwd_amd import attn_fwd
+from _gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+NK = (1 << 24) + 40
+NQ = 128
+# marked rows of V: (first row, last row, column, value)
+MARKS = [(40, 63, 3, 1.0),                      # the first tile's tail
+         ((1 << 23) + 5, (1 << 23) + 70, 17, 2.0),
+         ((1 << 24) - 3, (1 << 24) + 30, 64, 4.0),   # across 2^24
+         (NK - 10, NK - 1, 127, 8.0)]           # the last rows (seen by the last causal rows only)
+
+
+def inputs():
+    q = torch.randn(1, 4, NQ, D, generator=torch.Generator(device="cuda").manual_seed(5), device="cuda")
+    k = torch.zeros(1, 1, NK, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(1, 1, NK, D, dtype=torch.bfloat16, device="cuda")
+    for a, b, col, val in MARKS:
+        v[0, 0, a:b + 1, col] = val
+    return q.to(torch.bfloat16), k, v
+
+
+def expected(last_key: int):
+    """Output row and LSE of a query that sees keys 0..last_key."""
+    n = last_key + 1
+    o = np.zeros(D)
+    for a, b, col, val in MARKS:
+        seen = max(0, min(b, last_key) - a + 1)
+        o[col] += val * seen / n
+    return o, math.log(n)
+
+
+def check(o: torch.Tensor, lse: torch.Tensor, last_keys, label: str):
+    og = o[0].double().cpu().numpy()      # [Hq, NQ, D]
+    lg = lse[0].double().cpu().numpy()    # [Hq, NQ]
+    worst_rel, worst_lse = 0.0, 0.0
+    for i, lk in enumerate(last_keys):
+        o_ref, l_ref = expected(lk)
+        nz = o_ref != 0
+        for h in range(og.shape[0]):
+            assert np.all(og[h, i, ~nz] == 0.0), f"{label} row {i}: nonzero output where V is zero"
+            rel = np.abs(og[h, i, nz] - o_ref[nz]) / o_ref[nz]
+            worst_rel = max(worst_rel, float(rel.max()))
+            worst_lse = max(worst_lse, abs(lg[h, i] - l_ref))
+    say(f"[long keys] {label}: Nk {NK}, max relative error {worst_rel:.3e}, LSE {worst_lse:.3e}")
+    assert worst_rel <= 2.0 ** -8, f"{label}: relative error {worst_rel}"
+    assert worst_lse <= 1e-3, f"{label}: LSE error {worst_lse}"
+
+
+def test_prefill_keys_past_2_24_no_mask():
+    q, k, v = inputs()
+    o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="none")
+    torch.cuda.synchronize()
+    check(o, lse, [NK - 1] * NQ, "no mask")
+
+
+def test_prefill_keys_past_2_24_causal_bottom_right():
+    q, k, v = inputs()
+    o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="causal")
+    torch.cuda.synchronize()
+    check(o, lse, [NK - NQ + i for i in range(NQ)], "causal")
