@@ -6,14 +6,15 @@
 //   P = exp(S - LSE),  D = rowsum(dO o O),  dS = P o (dO V^T - D)
 //   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q
 //
-// Three passes, no atomics:
-//   prep   per query row: -LSE log2(e), D and the row's visible key interval
-//          (then, with a learned sink, a per-head reduction of its gradient
-//          -sum_i P_sink,i D_i in a fixed order);
+// Two passes, no atomics:
 //   dQ     one workgroup per (batch, query head, 128-row query tile), each
-//          wave owning 32 rows as in the forward; per 32-key tile it
-//          recomputes S^T = K Q^T and dP^T = V dO^T and accumulates
-//          dQ^T += K^T dS^T (the forward's O^T += V^T P^T with K and dS);
+//          wave owning 32 rows as in the forward.  It first writes each
+//          row's statistics to the workspace (-LSE log2(e), D and the row's
+//          visible key interval), then per 32-key tile recomputes
+//          S^T = K Q^T and dP^T = V dO^T and accumulates dQ^T += K^T dS^T
+//          (the forward's O^T += V^T P^T with K and dS); with a learned
+//          sink, a per-head reduction of its gradient -sum_i P_sink,i D_i
+//          in a fixed order follows;
 //   dK/dV  one workgroup per (batch, KV head, 128-key tile), each wave owning
 //          32 keys in registers; it streams 64-row query tiles of every query
 //          head of the group, recomputes S = Q K^T and dP = dO V^T with the
@@ -177,40 +178,9 @@ __device__ __forceinline__ PrefillParams mask_params(const BackwardParams& p) {
 
 }  // namespace
 
-// D / 8 threads per query row (8 columns each): D = dO . O, plus the row's
-// statistics for the two gradient passes.  256 / (D / 8) rows per workgroup.
-template <int D>
-__device__ __forceinline__ void bwd_prep_body(BackwardParams p) {
-    constexpr int TPR = D / 8;
-    const int t = threadIdx.x;
-    const long long rows = (long long)p.B * p.Hq * p.Nq;
-    const long long rg = (long long)blockIdx.x * (256 / TPR) + t / TPR;
-    float acc = 0.f;
-    if (rg < rows) {
-        const u32x4 a = *(const u32x4*)(p.o + rg * D + (t % TPR) * 8);
-        const u32x4 g = *(const u32x4*)(p.dO + rg * D + (t % TPR) * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
-    }
-#pragma unroll
-    for (int o = TPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (rg < rows && t % TPR == 0) {
-        const int i = (int)(rg % p.Nq);
-        const float L = p.lse[rg];
-        p.ws_d[rg] = acc;
-        p.ws_nl[rg] = L > -__builtin_inff() ? -L * kLog2e : 0.f;
-        const PrefillParams m = mask_params(p);
-        int lo, hi;
-        row_interval(m, i, lo, hi);
-        p.ws_lo[rg] = lo;
-        p.ws_hi[rg] = hi;
-    }
-}
-
 // The learned sink's gradient, dsink[h] = -sum over (batch, row) of
-// P_sink D with P_sink = exp(sink[h] - LSE), from the saved LSE and the prep
-// pass's D.  One workgroup per query head; every thread sums its rows in a
+// P_sink D with P_sink = exp(sink[h] - LSE), from the saved LSE and the D
+// that the dQ pass (the fp32 path: its prep pass) left in the workspace.  One workgroup per query head; every thread sums its rows in a
 // fixed order and the workgroup adds the partial sums in a fixed tree, so the
 // result is the same bit for bit on every run (no atomics).
 __global__ __launch_bounds__(256) void bwd_dsink_kernel(BackwardParams p) {
@@ -239,9 +209,6 @@ void launch_dsink(const BackwardParams& p, hipStream_t stream) {
     if (p.dsink == nullptr || p.Hq == 0) return;
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(p.Hq), dim3(256), 0, stream, p);
 }
-
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) { bwd_prep_body<128>(p); }
-__global__ __launch_bounds__(256) void bwd_prep_d64_kernel(BackwardParams p) { bwd_prep_body<64>(p); }
 
 // dQ: per 32-key tile, S^T = K Q^T, dP^T = V dO^T, dS = P (dP - D),
 // dQ^T += K^T dS^T.  At d = 128 the K tile is one DualSwizzle copy that
@@ -313,8 +280,32 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     bf16x8 qf[D / 16], df[D / 16];
     load_fragment<D>(p.q + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, qf);
     load_fragment<D>(p.dO + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, df);
-    const float nl = row_ok ? p.ws_nl[head_row + row] : -__builtin_inff();
-    const float Drow = row_ok ? p.ws_d[head_row + row] : 0.f;
+    // The row's statistics, which the dK/dV pass and the sink gradient read
+    // from the workspace: D = dO . O (this lane and lane ^ 32 hold the two
+    // halves of the row), -LSE log2 e (0 for a row that sees nothing) and
+    // the row's visible key interval.  Every row belongs to one workgroup
+    // of this pass, so nothing else computes them.
+    float nl, Drow;
+    {
+        bf16x8 of[D / 16];
+        load_fragment<D>(p.o + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, of);
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)df[kk][e], (float)of[kk][e], acc);
+        acc += __shfl_xor(acc, 32);
+        const float L = row_ok ? p.lse[head_row + row] : -__builtin_inff();
+        const float nlw = L > -__builtin_inff() ? -L * kLog2e : 0.f;
+        nl = row_ok ? nlw : -__builtin_inff();
+        Drow = row_ok ? acc : 0.f;
+        if (row_ok && lane < 32) {
+            p.ws_d[head_row + row] = acc;
+            p.ws_nl[head_row + row] = nlw;
+            p.ws_lo[head_row + row] = lo_i;
+            p.ws_hi[head_row + row] = hi_i;
+        }
+    }
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -774,19 +765,16 @@ int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
     p.ws_hi = (int32_t*)((char*)ws + 3 * stride);
     const dim3 wg(256), gq(p.B * p.Hq * p.num_q_tiles), gk(p.B * p.Hkv * p.num_k_tiles);
     if (rows > 0) {
-        const size_t rows_per_wg = 256 / (d / 8);   // the prep pass's D / 8 threads per row
-        const dim3 gp((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+        // the dQ pass also writes every row's statistics for the passes after it
         if (d == 128) {
-            hipLaunchKernelGGL(bwd_prep_kernel, gp, wg, 0, stream, p);
             if (mods) hipLaunchKernelGGL(bwd_dq_mod_kernel, gq, wg, 0, stream, p);
             else hipLaunchKernelGGL(bwd_dq_kernel, gq, wg, 0, stream, p);
         } else {
-            hipLaunchKernelGGL(bwd_prep_d64_kernel, gp, wg, 0, stream, p);
             if (mods) hipLaunchKernelGGL(bwd_dq_d64_mod_kernel, gq, wg, 0, stream, p);
             else hipLaunchKernelGGL(bwd_dq_d64_kernel, gq, wg, 0, stream, p);
         }
     }
-    launch_dsink(p, stream);   // after prep (it reads D); also with no rows, where it writes 0
+    launch_dsink(p, stream);   // after the dQ pass (it reads D); also with no rows, where it writes 0
     if ((long long)p.B * p.Hkv * p.num_k_tiles > 0) {
         if (d == 128) {
             if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, gk, wg, 0, stream, p);

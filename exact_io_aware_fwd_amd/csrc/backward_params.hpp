@@ -18,7 +18,7 @@ struct BackwardParams {
     uint16_t* dk;          // [B, Hkv, Nk, d]: summed over each group's query heads
     uint16_t* dv;
     float* dsink;          // [Hq] or null
-    // per-row statistics the prep pass writes, each [B, Hq, Nq]
+    // per-row statistics (written by the dQ pass, or by the fp32 path's prep pass), each [B, Hq, Nq]
     float* ws_nl;          // -LSE * log2(e) (0 for a row that sees nothing)
     float* ws_d;           // D = rowsum(dO o O)
     int32_t* ws_lo;        // visible key interval [lo, hi] of the row
@@ -40,7 +40,7 @@ struct BackwardParams {
 size_t backward_workspace_bytes(int B, int Hq, int Nq);
 int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream);   // d: 64 or 128
 int launch_backward_f32(BackwardParams p, int d, void* ws, hipStream_t stream);   // fp32 tensors, same workspace
-// dsink[h] from the saved LSE and the prep pass's D (no-op without a sink gradient)
+// dsink[h] from the saved LSE and the workspace's D (no-op without a sink gradient)
 void launch_dsink(const BackwardParams& p, hipStream_t stream);
 
 }  // namespace xattn

@@ -61,7 +61,6 @@ def test_pmc_plan_maps_dispatches_to_workloads():
              "decode_split_kernel<128, false>": "void xattn::decode_split_kernel<128, false>(xattn::DecodeParams)",
              "decode_combine_kernel<128>": "void xattn::decode_combine_kernel<128>(xattn::DecodeParams)",
              "paged_prefill_swz_kernel<false>": "void xattn::paged_prefill_swz_kernel<false>(xattn::PagedPrefillParams)",
-             "bwd_prep_kernel": "void xattn::bwd_prep_kernel(xattn::BwdParams)",
              "bwd_dq_kernel": "void xattn::bwd_dq_kernel(xattn::BwdParams)",
              "bwd_dkdv_kernel": "void xattn::bwd_dkdv_kernel(xattn::BwdParams)"}
     per[(str(did), "__amd_rocclr_copyBuffer")] = 1.0
