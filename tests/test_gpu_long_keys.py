@@ -84,3 +84,47 @@ def test_prefill_keys_past_2_24_causal_bottom_right():
     o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="causal")
     torch.cuda.synchronize()
     check(o, lse, [NK - NQ + i for i in range(NQ)], "causal")
+
+
+def test_backward_rows_past_2_24():
+    """The backward's Q and dO tiles over 2^24 + 40 query rows (one 128-key
+    tile, no mask).  With every key zero each row's P is 1/128 on every key
+    and its O is the mean of V, so (identical-keys closed form, then the
+    backward's definitions): dQ = 0; dV_j = sum_i dO_i / 128;
+    dK_j = scale / 128 * (sum_i q_i dO_i^T) (v_j - O), with O the bf16 mean of
+    V the kernel reads back.  Every query row reaches dV and dK, so a tile read
+    short or from the wrong rows moves them.  Bound: the backward tests'
+    relative Frobenius error 2e-2; dQ exactly zero."""
+    from exact_io_aware_fwd_amd import attn_bwd
+
+    nq, nk = (1 << 24) + 40, 128
+    g = torch.Generator(device="cuda").manual_seed(23)
+    q = torch.randn(1, 1, nq, D, generator=g, device="cuda").to(torch.bfloat16)
+    do = torch.randn(1, 1, nq, D, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(1, 1, nk, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.randn(1, 1, nk, D, generator=g, device="cuda").to(torch.bfloat16)
+    o_row = v[0, 0].double().mean(dim=0).to(torch.bfloat16)            # the forward's output of every row
+    o = o_row.view(1, 1, 1, D).expand(1, 1, nq, D).contiguous()
+    lse = torch.full((1, 1, nq), math.log(nk), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    dq, dk, dv, _ = attn_bwd(q, k, v, o, do, lse, scale=scale, mask="none")
+    torch.cuda.synchronize()
+
+    # references in fp64, a million rows at a time
+    col = torch.zeros(D, dtype=torch.float64, device="cuda")
+    M = torch.zeros(D, D, dtype=torch.float64, device="cuda")
+    for a in range(0, nq, 1 << 20):
+        qc, dc = q[0, 0, a:a + (1 << 20)].double(), do[0, 0, a:a + (1 << 20)].double()
+        col += dc.sum(dim=0)
+        M += qc.T @ dc
+    dv_ref = (col / nk).expand(nk, D)
+    dk_ref = (scale / nk) * (v[0, 0].double() - o_row.double()) @ M.T
+
+    def rel(x, ref):
+        return float(torch.linalg.norm(x[0, 0].double() - ref) / torch.linalg.norm(ref))
+
+    e_dv, e_dk = rel(dv, dv_ref), rel(dk, dk_ref)
+    nz = int(torch.count_nonzero(dq))
+    say(f"[long rows] backward: Nq {nq}, dV rel-fro {e_dv:.3e}, dK rel-fro {e_dk:.3e}, nonzero dQ {nz}")
+    assert nz == 0
+    assert e_dv <= 2e-2 and e_dk <= 2e-2
