@@ -148,8 +148,12 @@ def decode_bytes(c: dict) -> int:
 
 
 def source_digest() -> str:
+    """SHA-256 over the kernel sources' names and bytes (files only: a cache
+    directory beside them does not count)."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if not os.path.isfile(p):
+            continue
         h.update(os.path.basename(p).encode())
         h.update(open(p, "rb").read())
     return h.hexdigest()

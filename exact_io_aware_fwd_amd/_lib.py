@@ -26,7 +26,8 @@ class AttnMask(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("doc_offsets", ctypes.c_void_p), ("num_docs", ctypes.c_int32),
                 ("sink_tokens", ctypes.c_int32), ("sink_logits", ctypes.c_void_p),
-                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
+                ("soft_exp2", ctypes.c_int32)]
 
 
 _lib = None

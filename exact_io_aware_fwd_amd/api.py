@@ -68,7 +68,8 @@ def _slopes_ptr(alibi_slopes: torch.Tensor | None, Hq: int):
 
 def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | None = None,
               sink_tokens: int = 0, sink_logits: torch.Tensor | None = None, Hq: int = 0,
-              softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None) -> _lib.AttnMask:
+              softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
+              soft_exp2: int = 0) -> _lib.AttnMask:
     _need(mask in _lib.MASK_KINDS, f"unknown mask {mask!r}")
     m = _lib.AttnMask()
     m.kind = _lib.MASK_KINDS[mask]
@@ -77,6 +78,7 @@ def make_mask(mask: str = "none", window: int = 0, doc_offsets: torch.Tensor | N
     m.sink_logits = _sink_ptr(sink_logits, Hq)
     m.softcap = float(softcap)
     m.alibi_slopes = _slopes_ptr(alibi_slopes, Hq)
+    m.soft_exp2 = int(soft_exp2)
     if mask == "document":
         _need(doc_offsets is not None and doc_offsets.dtype == torch.int32 and doc_offsets.is_cuda
               and doc_offsets.is_contiguous(), "document mask needs int32 device doc_offsets")
@@ -93,10 +95,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
              sink_tokens: int = 0, sink_logits: torch.Tensor | None = None,
              softcap: float = 0.0, alibi_slopes: torch.Tensor | None = None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None, with_lse: bool = True,
-             stream=None):
+             soft_exp2: int = 0, stream=None):
     """Attention forward: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> (o [B,Hq,Nq,d], lse [B,Hq,Nq] fp32).
     sink_tokens (window mask) and sink_logits [Hq] fp32 are the optional attention sinks;
-    softcap and alibi_slopes [Hq] fp32 the optional score modifications (bf16 only)."""
+    softcap and alibi_slopes [Hq] fp32 the optional score modifications (bf16 only).
+    soft_exp2 (0, 2 or 4; bf16, d = 128, no score modifications): that many of every 8
+    softmax weights take a software 2^x on the FMA units instead of the hardware one."""
     _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-d [B, H, N, d]")
     _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "dtype must be bf16 or fp32, same for q/k/v")
     _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous device tensors")
@@ -114,7 +118,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     elif lse is not None:
         _check_buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
-    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes)
+    m = make_mask(mask, window, doc_offsets, sink_tokens, sink_logits, Hq, softcap, alibi_slopes, soft_exp2)
     st = _lib.lib().attn_fwd(ctypes_ptr(q), ctypes_ptr(k), ctypes_ptr(v), ctypes_ptr(out),
                              None if lse is None else ctypes_ptr(lse),
                              B, Hq, Hkv, Nq, Nk, d, float(scale), m, _DTYPES[q.dtype], _stream(stream))

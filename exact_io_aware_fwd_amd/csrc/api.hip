@@ -68,7 +68,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (!sinks_ok(mask) || !mods_ok(mask)) return ATTN_ERR_INVALID_ARGUMENT;
     if (!(scale == scale) || scale <= 0.f || scale == __builtin_inff()) return ATTN_ERR_INVALID_ARGUMENT;
     if (Hkv == 0 ? Hq != 0 : (Hq % Hkv) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+    if (mask.soft_exp2 != 0 && mask.soft_exp2 != 2 && mask.soft_exp2 != 4) return ATTN_ERR_INVALID_ARGUMENT;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (mask.soft_exp2 != 0 &&
+        (d != 128 || dtype != ATTN_DTYPE_BF16 || mask.softcap > 0.f || mask.alibi_slopes != nullptr))
+        return ATTN_ERR_UNSUPPORTED;
     if (Nq > kMaxSeq || Nk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hq * Nq == 0) return ATTN_OK;  // nothing to write
     if (q == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARGUMENT;
@@ -94,6 +98,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.sink_logits = mask.sink_logits;
     p.softcap = mask.softcap;
     p.alibi_slopes = mask.alibi_slopes;
+    p.soft_exp2 = mask.soft_exp2;
 
     if (dtype == ATTN_DTYPE_BF16)
         xattn::launch_prefill_bf16(p, d, stream);

@@ -20,6 +20,7 @@
 // Softmax runs in base 2: scores are scaled by scale*log2(e) with one FMA that
 // also subtracts the running max, then v_exp_f32.  The division by the row sum
 // happens once at the end (delayed normalisation, FlashAttention-2 section).
+#include "exp2_poly.hpp"
 #include "prefill_tiles.hpp"
 
 namespace xattn {
@@ -253,7 +254,10 @@ __device__ __forceinline__ float prepare_tile(PrefillBf16State<D>& st, f32x16 (&
 // points at 4 columns c0+4q.. of key row k, and lane i receives column
 // c0+i of those 4 rows.  Rows are picked so the 8 keys a lane holds are the
 // ones its P^T operand slots hold.
-template <int D, class T>
+//
+// SOFT: the first SOFT of the 8 weights a lane computes per 16-key block take
+// the software 2^x (soft_exp2, FMA units), the rest v_exp_f32.
+template <int D, int SOFT, class T>
 __device__ __forceinline__ void softmax_pv(PrefillBf16State<D>& st, f32x16 (&s)[2], const T& tl, float scale_log2,
                                            float m_use) {
     using C = PrefillBf16Cfg<D>;
@@ -264,7 +268,8 @@ __device__ __forceinline__ void softmax_pv(PrefillBf16State<D>& st, f32x16 (&s)[
         const int jb = kb >> 1, h = (kb & 1) * 8;
 #pragma unroll
         for (int r = h; r < h + 8; ++r) {
-            s[jb][r] = fast_exp2(__builtin_fmaf(s[jb][r], scale_log2, -m_use));
+            const float x = __builtin_fmaf(s[jb][r], scale_log2, -m_use);
+            s[jb][r] = r - h < SOFT ? soft_exp2(x) : fast_exp2(x);
             fs[(r & 1) + 2 * jb] += s[jb][r];
         }
         u32x4 w;
@@ -291,7 +296,8 @@ __device__ __forceinline__ void softmax_pv(PrefillBf16State<D>& st, f32x16 (&s)[
 // S^T = K Q^T, mask, online softmax and O^T += V^T P^T for one wave and one
 // key tile resident in LDS, laid out as T says.  MODS: the scores first go
 // through the score modifications sm (qpos: this lane's query position).
-template <int D, bool MODS = false, class T>
+// SOFT: weights from the software 2^x, as in softmax_pv.
+template <int D, bool MODS = false, int SOFT = 0, class T>
 __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, int n0,
                                           bool full, int lo_i, int hi_i, int sink_end, float scale_log2, int lane,
                                           const ScoreMod& sm = ScoreMod{}, int qpos = 0) {
@@ -300,7 +306,7 @@ __device__ __forceinline__ void tile_step(PrefillBf16State<D>& st, const T& tl, 
     qk_tile<D>(s, st, tl);
     order_reads_ahead<2 * C::DK, 1, 4>();
     const float m_use = prepare_tile<D, MODS>(st, s, n0, full, lo_i, hi_i, sink_end, scale_log2, lane, sm, qpos);
-    softmax_pv<D>(st, s, tl, scale_log2, m_use);
+    softmax_pv<D, SOFT>(st, s, tl, scale_log2, m_use);
     interleave_weights_products<4 * C::CB, 40, 6>();
 }
 
@@ -328,7 +334,7 @@ __device__ __forceinline__ void load_swz_tile_async(const uint16_t* __restrict__
 #endif
 }
 
-template <int D, bool SINKS, bool MODS>
+template <int D, bool SINKS, bool MODS, int SOFT = 0>
 __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
     using C = PrefillBf16Cfg<D>;
     // Head dim 128 keeps its K/V tiles unpadded and swizzled (16 KiB each,
@@ -447,8 +453,8 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
                 if constexpr (SWZ) {
                     stl.k = kc;
                     stl.v = vc;
-                    tile_step<D, MODS>(st, stl, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane, sm,
-                                       row + p.Nk - p.Nq);
+                    tile_step<D, MODS, SOFT>(st, stl, n0, full, lo_i, hi_i, sink_end, p.scale_log2, lane, sm,
+                                             row + p.Nk - p.Nq);
                 } else {
                     tile_step<D, MODS>(st, PaddedTiles<D>{kc + kbase, vc + vbase}, n0, full, lo_i, hi_i, sink_end,
                                        p.scale_log2, lane, sm, row + p.Nk - p.Nq);
@@ -495,6 +501,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p) {
 template <int D, bool SINKS>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_mod_kernel(PrefillParams p) {
     prefill_bf16_body<D, SINKS, true>(p);
+}
+
+// d = 128 with SOFT of each lane's 8 weights per 16-key block from the
+// software 2^x (kernels of their own, so the plain kernel's code does not
+// change)
+template <bool SINKS, int SOFT>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_soft_kernel(PrefillParams p) {
+    prefill_bf16_body<128, SINKS, false, SOFT>(p);
 }
 
 // ------------------------------------------------------------------------
@@ -958,7 +972,15 @@ int launch_prefill_bf16(const PrefillParams& p0, int d, hipStream_t stream) {
     const bool sinks = p.sink_end > 0;
     const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
     const dim3 g(blocks), wg(256);
-    if (d == 128) {
+    if (d == 128 && p.soft_exp2 != 0) {  // accepted only without score modifications
+        if (p.soft_exp2 == 2) {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_soft_kernel<true, 2>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_soft_kernel<false, 2>), g, wg, 0, stream, p);
+        } else {
+            if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_soft_kernel<true, 4>), g, wg, 0, stream, p);
+            else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_soft_kernel<false, 4>), g, wg, 0, stream, p);
+        }
+    } else if (d == 128) {
         if (mods) {
             if (sinks) hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<128, true>), g, wg, 0, stream, p);
             else hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_bf16_mod_kernel<128, false>), g, wg, 0, stream, p);

@@ -110,6 +110,11 @@ typedef struct {
     const float* sink_logits;   /* NULL or device [Hq]: learned sink logit per query head */
     float softcap;              /* > 0: scores become softcap * tanh(score / softcap); 0: off */
     const float* alibi_slopes;  /* NULL or device [Hq]: score += slope * (key - query position) */
+    int32_t soft_exp2;          /* attn_fwd only, a performance option: 0 (the default) takes every
+                                   softmax weight's 2^x from the hardware exponential; 2 or 4 take
+                                   that many of each lane's 8 weights per 16-key block (a quarter
+                                   or half) from a software 2^x on the FMA units instead (see
+                                   below).  The other entry points ignore it. */
 } attn_mask;
 
 /*
@@ -135,6 +140,15 @@ typedef struct {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              attn_mask mask, int dtype, hipStream_t stream);
+/*
+ * mask.soft_exp2 (FlashAttention-4's software exponential, "Attention Is the
+ * Bottleneck", FlashAttention-4 section): 2^x as 2^rint(x) times a degree-4
+ * polynomial of the remainder, relative error at most 2.7e-6.  Supported for
+ * bf16, d = 128 and no score modifications (ATTN_ERR_UNSUPPORTED otherwise);
+ * values other than 0, 2 and 4 are ATTN_ERR_INVALID_ARGUMENT.  On MI355X it is
+ * measured 8-17 % slower than the hardware exponential, which is why 0 is the
+ * default.
+ */
 
 /*
  * attn_paged_decode_workspace_size — bytes of scratch device memory that

@@ -40,8 +40,9 @@ def test_status_strings():
 
 
 def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.1,
-        kind=0, window=0, doc=None, num_docs=0, dtype=1, sink_tokens=0, sinks=None, softcap=0.0, alibi=None):
-    m = _lib.AttnMask(kind, window, doc, num_docs, sink_tokens, sinks, softcap, alibi)
+        kind=0, window=0, doc=None, num_docs=0, dtype=1, sink_tokens=0, sinks=None, softcap=0.0, alibi=None,
+        soft=0):
+    m = _lib.AttnMask(kind, window, doc, num_docs, sink_tokens, sinks, softcap, alibi, soft)
     return _lib.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, m, dtype, None)
 
 
@@ -57,6 +58,10 @@ def fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=16, Nk=16
     (dict(sinks=FAKE + 2), 1), (dict(kind=2, window=8, sink_tokens=4, d=96), 2),
     (dict(softcap=-1.0), 1), (dict(softcap=float("nan")), 1), (dict(softcap=float("inf")), 1),
     (dict(alibi=FAKE + 2), 1), (dict(softcap=-1.0, dtype=0), 1), (dict(softcap=5.0, d=96), 2),
+    # the software 2^x: 0, 2 or 4; only bf16, d = 128, no score modifications
+    (dict(soft=1), 1), (dict(soft=3), 1), (dict(soft=8), 1), (dict(soft=-2), 1), (dict(soft=3, d=64), 1),
+    (dict(soft=2, d=64), 2), (dict(soft=4, dtype=0), 2), (dict(soft=2, softcap=5.0), 2),
+    (dict(soft=4, alibi=FAKE), 2), (dict(soft=2, d=96), 2),
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
@@ -67,6 +72,7 @@ def test_fwd_empty_problems_are_noops():
     assert fwd(q=None, k=None, v=None, o=None, lse=None, Nq=0) == 0
     assert fwd(q=None, k=None, v=None, o=None, lse=None, B=0) == 0
     assert fwd(q=None, k=None, v=None, o=None, lse=None, Hq=0, Hkv=0) == 0
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, Nq=0, soft=4) == 0
 
 
 def dec(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, S=2, Hq=8, Hkv=2, d=128, page=16,
