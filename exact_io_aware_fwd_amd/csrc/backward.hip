@@ -153,15 +153,55 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[D /
         }
 }
 
+// The same rows through this wave's LDS staging area `stg` (32 rows of
+// 2 D + 16 bytes, the padding spreading the rows' writes over the banks):
+// each lane writes its pieces of its row, then every store writes whole
+// rows, 16 bytes per lane (row stores of 8 bytes per lane spread over 32
+// rows took about 3500 cycles per d x 32 tile).  dst is row 0; rows at or
+// past `rows` are not written.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(uint16_t* dst, int rows, const f32x16 (&acc)[D / 32], float mul,
+                                                  int lane, uint8_t* stg) {
+    constexpr int RB = 2 * D + 16;   // staged row stride in bytes
+    constexpr int CPR = 2 * D / 16;  // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR;    // rows per store
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[cb][4 * gq + 0] * mul, acc[cb][4 * gq + 1] * mul);
+            w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * mul, acc[cb][4 * gq + 3] * mul);
+            *(u32x2*)(stg + (lane & 31) * RB + (cb * 32 + 8 * gq + 4 * (lane >> 5)) * 2) = w;
+        }
+    // the wave reads what its other lanes wrote
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 32 / RPS; ++j) {
+        const int row = j * RPS + lane / CPR, c = lane % CPR;
+        const u32x4 v = *(const u32x4*)(stg + row * RB + c * 16);
+        if (row < rows) *(u32x4*)(dst + (size_t)row * D + c * 8) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // The B operand fragment of a row held in registers (query row for dQ, key
 // for dK/dV): chunks (lane >> 5) * 8 .. + 8 of every 16-wide head-dim step.
+// rowp is a row that exists even where !ok (the caller's row 0 then); it is
+// read either way and the fragment zeroed after, with no branch per load.
 template <int D>
 __device__ __forceinline__ void load_fragment(const uint16_t* rowp, bool ok, int lane, bf16x8 (&f)[D / 16]) {
+    u32x4 w[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 w = ok ? *(const u32x4*)(rowp + kk * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
-        f[kk] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) w[kk] = *(const u32x4*)(rowp + kk * 16 + (lane >> 5) * 8);
+    const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        f[kk] = __builtin_bit_cast(bf16x8, u32x4{w[kk][0] & keep, w[kk][1] & keep, w[kk][2] & keep, w[kk][3] & keep});
 }
 
 __device__ __forceinline__ PrefillParams mask_params(const BackwardParams& p) {
@@ -464,6 +504,8 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     // per tile row: -LSE log2 e, D, lo, hi (256 bytes each)
     __shared__ __attribute__((aligned(1024))) uint8_t st0[4 * BQ * 4];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[4 * BQ * 4];
+    // each wave's dK and dV rows on their way out
+    __shared__ __attribute__((aligned(16))) uint8_t stage_out[4 * 32 * (2 * D + 16)];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -490,34 +532,11 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         dv[cb] = f32x16{};
     }
 
-    // Query rows that see any key of [k0, k_last]: from the first row whose
-    // interval reaches k0 to the last whose interval starts at or before
-    // k_last (every later row, when sink keys are in the tile).  Both ends
-    // are monotone in the row, so two binary searches find them.
+    // Query rows that see any key of [k0, k_last] (in closed form but for
+    // document masks: two scalar binary searches here took about 4500 cycles
+    // of a workgroup that runs alone on its CU)
     int first = p.Nq, last = -1;
-    {
-        int a = 0, z = p.Nq;
-        while (a < z) {
-            const int mid = (a + z) >> 1;
-            int l, h;
-            row_interval(m, mid, l, h);
-            if (h >= k0) z = mid; else a = mid + 1;
-        }
-        first = a;
-        if (k0 < p.sink_end) {
-            last = p.Nq - 1;
-        } else {
-            a = -1;
-            z = p.Nq - 1;
-            while (a < z) {
-                const int mid = (a + z + 1) >> 1;
-                int l, h;
-                row_interval(m, mid, l, h);
-                if (l <= k_last) a = mid; else z = mid - 1;
-            }
-            last = a;
-        }
-    }
+    if (k0 < p.Nk) query_rows_seeing(m, k0, k_last, first, last);
     const int qt_first = first / BQ;
     const int ntq = (first <= last && k0 < p.Nk) ? last / BQ - qt_first + 1 : 0;
     const int n_iter = ntq * p.group;
@@ -739,9 +758,10 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
             if (it + 1 < n_iter) stage(it + 1, qr1, qt1, dr1, dt1, st1, qr0, qt0, dr0, dt0, st0);
         }
     }
-    if (key_ok) {
-        store_row<D>(p.dk + (kv_head + key) * D, dk, p.scale, lane);
-        store_row<D>(p.dv + (kv_head + key) * D, dv, 1.f, lane);
+    if (k0w < p.Nk) {
+        uint8_t* stg = stage_out + wave * 32 * (2 * D + 16);
+        store_rows_staged<D>(p.dk + (kv_head + k0w) * D, p.Nk - k0w, dk, p.scale, lane, stg);
+        store_rows_staged<D>(p.dv + (kv_head + k0w) * D, p.Nk - k0w, dv, 1.f, lane, stg);
     }
 }
 

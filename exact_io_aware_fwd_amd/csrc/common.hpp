@@ -99,7 +99,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // First key position of the document that holds key position `pos` (pos >= 0).
-__device__ __forceinline__ int doc_start(const int32_t* off, int num_docs, int pos) {
+__host__ __device__ __forceinline__ int doc_start(const int32_t* off, int num_docs, int pos) {
     int lo = 0, hi = num_docs - 1;  // answer t in [0, num_docs-1] with off[t] <= pos
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -112,7 +112,7 @@ __device__ __forceinline__ int doc_start(const int32_t* off, int num_docs, int p
 // mask kind; an empty row has lo > hi.  Query i sits at key position
 // pos = i + Nk - Nq.  Both ends are non-decreasing in i, which is what lets a
 // tile of rows bound its key range by its first and last row.
-__device__ __forceinline__ void row_interval(const PrefillParams& p, int i, int& lo, int& hi) {
+__host__ __device__ __forceinline__ void row_interval(const PrefillParams& p, int i, int& lo, int& hi) {
     if (i < 0 || i >= p.Nq) { lo = p.Nk; hi = -1; return; }
     const int pos = i + p.Nk - p.Nq;
     if (p.mask_kind == kMaskNone) { lo = 0; hi = p.Nk - 1; return; }
@@ -125,6 +125,42 @@ __device__ __forceinline__ void row_interval(const PrefillParams& p, int i, int&
         lo = lo > 0 ? lo : 0;
     } else {
         lo = doc_start(p.doc_offsets, p.num_docs, pos);
+    }
+}
+
+// Query rows that see some key of [k0, k_last] (0 <= k0 <= k_last < Nk), as
+// the range [first, last] (empty when first > last): from the first row whose
+// interval reaches k0 (hi >= k0) to the last row whose interval starts at or
+// before k_last (lo <= k_last), or every later row when sink keys lie in the
+// range.  Both ends are monotone in the row.  With row = pos + Nq - Nk, a
+// masked row's end min(pos, Nk - 1) reaches k0 exactly when pos >= k0, and a
+// window row's start max(pos - W + 1, 0) is at most k_last exactly when
+// pos <= k_last + W - 1; so only document masks, whose starts come from the
+// offsets, search the rows.
+__host__ __device__ __forceinline__ void query_rows_seeing(const PrefillParams& p, int k0, int k_last, int& first,
+                                                           int& last) {
+    const int shift = p.Nq - p.Nk;
+    if (p.mask_kind == kMaskNone) {
+        first = 0;
+        last = p.Nq - 1;
+        return;
+    }
+    first = k0 + shift;
+    first = first < 0 ? 0 : (first > p.Nq ? p.Nq : first);
+    if (k0 < p.sink_end || p.mask_kind == kMaskCausal) {
+        last = p.Nq - 1;
+    } else if (p.mask_kind == kMaskWindow) {
+        last = k_last + p.window - 1 + shift;
+        last = last < -1 ? -1 : (last > p.Nq - 1 ? p.Nq - 1 : last);
+    } else {
+        int a = -1, z = p.Nq - 1;
+        while (a < z) {
+            const int mid = (a + z + 1) >> 1;
+            int l, h;
+            row_interval(p, mid, l, h);
+            if (l <= k_last) a = mid; else z = mid - 1;
+        }
+        last = a;
     }
 }
 
