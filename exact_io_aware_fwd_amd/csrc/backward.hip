@@ -138,27 +138,13 @@ __device__ __forceinline__ void rows_times(const uint8_t* rl, const bf16x8 (&bf)
     order_operand_reads<D / 8, 1, 4>();
 }
 
-// Store a d x 32 accumulator (column = this lane's row or key) as one bf16
-// row of d values, times `mul`.
-template <int D>
-__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int lane) {
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[cb][4 * gq + 0] * mul, acc[cb][4 * gq + 1] * mul);
-            w[1] = pack_bf16x2(acc[cb][4 * gq + 2] * mul, acc[cb][4 * gq + 3] * mul);
-            *(u32x2*)(dst + cb * 32 + 8 * gq + 4 * (lane >> 5)) = w;
-        }
-}
-
-// The same rows through this wave's LDS staging area `stg` (32 rows of
-// 2 D + 16 bytes, the padding spreading the rows' writes over the banks):
-// each lane writes its pieces of its row, then every store writes whole
-// rows, 16 bytes per lane (row stores of 8 bytes per lane spread over 32
-// rows took about 3500 cycles per d x 32 tile).  dst is row 0; rows at or
-// past `rows` are not written.
+// Store a wave's d x 32 accumulator (column = this lane's row or key, 32
+// rows) as bf16 rows of d values, times `mul`, through the wave's LDS
+// staging area `stg` (32 rows of 2 d + 16 bytes, the padding spreading the
+// rows' writes over the banks): each lane writes its pieces of its row, then
+// every store writes whole rows, 16 bytes per lane (stores of 8 bytes per
+// lane straight from the accumulator, spread over 32 rows, took about 3500
+// cycles per tile).  dst is row 0; rows at or past `rows` are not written.
 template <int D>
 __device__ __forceinline__ void store_rows_staged(uint16_t* dst, int rows, const f32x16 (&acc)[D / 32], float mul,
                                                   int lane, uint8_t* stg) {
@@ -291,6 +277,8 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t kr1[RT];
     __shared__ __attribute__((aligned(1024))) uint8_t kt1_[TT];
     __shared__ __attribute__((aligned(1024))) uint8_t vr1[RT];
+    // each wave's dQ rows on their way out
+    __shared__ __attribute__((aligned(16))) uint8_t stage_out[4 * 32 * (2 * D + 16)];
     uint8_t* kt0 = SWZ ? kr0 : kt0_;
     uint8_t* kt1 = SWZ ? kr1 : kt1_;
 
@@ -316,36 +304,17 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
     row_interval(m, w_last, lo_w_last, hi_w_last);
     const bool wave_has_rows = w0 < p.Nq;
 
+    // Every load of the prologue (the row's LSE, the Q, dO and O fragments,
+    // and below the first K/V tile) is issued before the first wait on any of
+    // them: issued one after another's use, their round trips added up to
+    // about 7000 cycles per workgroup.
     const size_t head_row = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-    bf16x8 qf[D / 16], df[D / 16];
+    const float L = p.lse[head_row + (row_ok ? row : 0)];
+    bf16x8 qf[D / 16], df[D / 16], of[D / 16];
     load_fragment<D>(p.q + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, qf);
     load_fragment<D>(p.dO + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, df);
-    // The row's statistics, which the dK/dV pass and the sink gradient read
-    // from the workspace: D = dO . O (this lane and lane ^ 32 hold the two
-    // halves of the row), -LSE log2 e (0 for a row that sees nothing) and
-    // the row's visible key interval.  Every row belongs to one workgroup
-    // of this pass, so nothing else computes them.
-    float nl, Drow;
-    {
-        bf16x8 of[D / 16];
-        load_fragment<D>(p.o + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, of);
-        float acc = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)df[kk][e], (float)of[kk][e], acc);
-        acc += __shfl_xor(acc, 32);
-        const float L = row_ok ? p.lse[head_row + row] : -__builtin_inff();
-        const float nlw = L > -__builtin_inff() ? -L * kLog2e : 0.f;
-        nl = row_ok ? nlw : -__builtin_inff();
-        Drow = row_ok ? acc : 0.f;
-        if (row_ok && lane < 32) {
-            p.ws_d[head_row + row] = acc;
-            p.ws_nl[head_row + row] = nlw;
-            p.ws_lo[head_row + row] = lo_i;
-            p.ws_hi[head_row + row] = hi_i;
-        }
-    }
+    load_fragment<D>(p.o + (head_row + (row_ok ? row : 0)) * D, row_ok, lane, of);
+    float nl = 0.f, Drow = 0.f;   // set below, once the first K/V copy is issued
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -451,14 +420,39 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
         order_operand_reads<D / 16, 2, 2>();
     };
 
+    if (tr.n > 0) copy(tile_of(tr, 0), kr0, kt0, vr0);
+    // The row's statistics, which the dK/dV pass and the sink gradient read
+    // from the workspace: D = dO . O (this lane and lane ^ 32 hold the two
+    // halves of the row), -LSE log2 e (0 for a row that sees nothing) and
+    // the row's visible key interval.  Every row belongs to one workgroup
+    // of this pass, so nothing else computes them.
+    {
+        float dsum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)df[kk][e], (float)of[kk][e], dsum);
+        dsum += __shfl_xor(dsum, 32);
+        const float Lr = row_ok ? L : -__builtin_inff();
+        const float nlw = Lr > -__builtin_inff() ? -Lr * kLog2e : 0.f;
+        nl = row_ok ? nlw : -__builtin_inff();
+        Drow = row_ok ? dsum : 0.f;
+        if (row_ok && lane < 32) {
+            p.ws_d[head_row + row] = dsum;
+            p.ws_nl[head_row + row] = nlw;
+            p.ws_lo[head_row + row] = lo_i;
+            p.ws_hi[head_row + row] = hi_i;
+        }
+    }
     if (tr.n > 0) {
-        copy(tile_of(tr, 0), kr0, kt0, vr0);
         for (int it = 0; it < tr.n; it += 2) {
             stage(it, kr0, kt0, vr0, kr1, kt1, vr1);
             if (it + 1 < tr.n) stage(it + 1, kr1, kt1, vr1, kr0, kt0, vr0);
         }
     }
-    if (row_ok) store_row<D>(p.dq + (head_row + row) * D, acc, p.scale, lane);
+    if (wave_has_rows)
+        store_rows_staged<D>(p.dq + (head_row + w0) * D, p.Nq - w0, acc, p.scale, lane,
+                             stage_out + wave * 32 * (2 * D + 16));
 }
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) { bwd_dq_body<128, false>(p); }
