@@ -351,6 +351,11 @@ __device__ __forceinline__ void bwd_dq_body(BackwardParams p) {
                      uint8_t* vrn) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of this tile landed
         __syncthreads();
+        // Two workgroups share a CU (dispatched num_cus apart); they take the
+        // higher wave priority in turn, tile by tile, as the forward does
+        // (C2 backward 307-310 -> 304-306 us in alternated timings).
+        if (((it + (int)blockIdx.x / p.num_cus) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if (it + 1 < tr.n) copy(tile_of(tr, it + 1), krn, ktn, vrn);
         const int n0 = tile_of(tr, it) * C::BN;
         const bool active = wave_has_rows && n0 <= hi_w_last && (n0 + C::BN - 1 >= lo_w_first || n0 < p.sink_end);
@@ -771,6 +776,7 @@ size_t backward_workspace_bytes(int B, int Hq, int Nq) {
 
 int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
     const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+    p.num_cus = device_cus();
     const bool mods = p.softcap > 0.f || p.alibi_slopes != nullptr;
     const size_t stride = ((rows * 4 + 255) / 256) * 256;
     p.ws_nl = (float*)ws;

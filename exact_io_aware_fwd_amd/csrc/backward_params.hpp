@@ -35,6 +35,7 @@ struct BackwardParams {
     const float* alibi_slopes; // [Hq] or null: score += slope * (key - query position)
     int num_q_tiles;       // 128-row query tiles (dQ pass)
     int num_k_tiles;       // 128-key tiles (dK/dV pass)
+    int num_cus;           // compute units of the device (the dQ pass's priority phase)
 };
 
 size_t backward_workspace_bytes(int B, int Hq, int Nq);

@@ -21,6 +21,9 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, workgroups dealt roun
 
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 3 };
 
+// Compute units of the current device (read once per process; host code).
+int device_cus();
+
 // Arguments of one prefill launch (already validated on the host).
 struct PrefillParams {
     const void* q;

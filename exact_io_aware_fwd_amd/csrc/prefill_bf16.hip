@@ -946,7 +946,7 @@ int launch_paged_prefill_bf16(const PagedPrefillParams& p, int d, hipStream_t st
 int prefill_bf16_rows_per_block() { return PrefillBf16Cfg<128>::BM; }
 
 // Compute units of the current device (read once per process).
-static int device_cus() {
+int device_cus() {
     static int cus = 0;
     if (cus == 0) {
         int dev = 0, n = 0;
