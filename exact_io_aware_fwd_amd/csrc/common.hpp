@@ -46,6 +46,7 @@ struct PrefillParams {
     float softcap;             // > 0: score -> softcap * tanh(score / softcap); 0: off
     const float* alibi_slopes; // [Hq] or null: score += slope * (key - query position)
     int soft_exp2 = 0;         // 0, 2 or 4: weights per lane and 16-key block from the software 2^x
+    int num_cus = 256;         // compute units of the device (the wave-priority phase)
 };
 
 // Arguments of one chunked-prefill launch over the paged cache (validated on

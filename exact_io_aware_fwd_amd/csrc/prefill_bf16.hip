@@ -441,7 +441,10 @@ __device__ __forceinline__ void prefill_bf16_body(PrefillParams p) {
             // per tile and ended about 14 us after the first half (workgroup
             // timestamps).  Handing the higher priority to the two halves in
             // turn, tile by tile, evens them out: C2 181 K -> 174 K cycles.
-            if (((it + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+            // The phase is the dispatch round (workgroups num_cus apart share
+            // a CU first), which for C2 is the grid's half; for the
+            // multi-round configs it took C3b from 167-171 to 164-165 us.
+            if (((it + (int)blockIdx.x / p.num_cus) & 1) != 0) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
             // (issuing these copies one or two at a time between the S^T
             // products, or after them, was 3-6 % slower than this burst)
@@ -967,6 +970,7 @@ int launch_prefill_bf16(const PrefillParams& p0, int d, hipStream_t stream) {
     // pairing was then slower (C3a +6 % cycles; C2 -2 %).
     const long long unpaired = (long long)p.B * p.Hq * p.num_q_tiles;
     const bool pair = p.mask_kind == kMaskCausal && p.num_q_tiles > 1 && unpaired <= 2LL * 2 * device_cus();
+    p.num_cus = device_cus();
     p.q_tile_pairs = pair ? (p.num_q_tiles + 1) / 2 : 0;
     const int blocks = p.B * p.Hq * (p.q_tile_pairs > 0 ? p.q_tile_pairs : p.num_q_tiles);
     const bool sinks = p.sink_end > 0;
