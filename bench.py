@@ -72,7 +72,7 @@ LEG_KERNELS = {
     "c3b": ["prefill_bf16_kernel<128, false>"], "c4": ["prefill_bf16_kernel<128, false>"],
     "c5": ["decode_split_kernel<128, false>", "decode_combine_kernel<128>"],
     "c6": ["paged_prefill_swz_kernel<false>"],
-    "bwd_c2": ["bwd_dq_kernel", "bwd_dkdv_kernel"],
+    "bwd_c2": ["bwd_dq_kernel", "bwd_dkdv2_kernel"],
 }
 LEG_WORKLOAD = {"c2": PREFILL_LEGS["c2"], "c3a": PREFILL_LEGS["c3a"], "c3b": PREFILL_LEGS["c3b"],
                 "c4": PREFILL_LEGS["c4"], "c5": DECODE_CONFIG, "c6": CHUNKED_CONFIG,

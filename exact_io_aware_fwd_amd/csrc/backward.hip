@@ -15,11 +15,13 @@
 //          (the forward's O^T += V^T P^T with K and dS); with a learned
 //          sink, a per-head reduction of its gradient -sum_i P_sink,i D_i
 //          in a fixed order follows;
-//   dK/dV  one workgroup per (batch, KV head, 128-key tile), each wave owning
-//          32 keys in registers; it streams 64-row query tiles of every query
-//          head of the group, recomputes S = Q K^T and dP = dO V^T with the
-//          keys as the accumulator columns, and accumulates dV^T += dO^T P
-//          and dK^T += Q^T dS.
+//   dK/dV  one workgroup per (batch, KV head, 128-key tile); it streams
+//          64-row query tiles of every query head of the group, recomputes
+//          S = Q K^T and dP = dO V^T with the keys as the accumulator
+//          columns, and accumulates dV^T += dO^T P and dK^T += Q^T dS.  At
+//          d = 128 two waves on one SIMD share each 32-key block (one holds
+//          K and dV, the other V and dK, the weights handed over in LDS,
+//          bwd_dkdv2_kernel); at d = 64 one wave owns each block.
 // At d = 128 a tile that one product reads by rows and another transposed
 // (Q and dO in the dK/dV pass, K in the dQ pass) is one swizzled copy that
 // both reads use without bank conflicts (DualSwizzle); at d = 64 such tiles
@@ -92,6 +94,20 @@ struct DualSwizzle {
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kb * 4096 + tr1[cb]));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    }
+    // the same with eight waves sharing the copies (blocks wave8 + 8 j; init
+    // took wave8 & 3, the block index modulo 4 that the swizzle uses)
+    template <int NB>
+    __device__ __forceinline__ void copy8(const uint16_t* src, int rows, uint8_t* lds, int wave8) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)src, (short)0, (int)tile_range_bytes<128>(rows, NB * 4), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < NB / 8; ++j) {
+            const int blk = wave8 + 8 * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 1024), 16, cpo, blk * 1024, 0, 0);
+        }
+#endif
     }
     // this wave's copies of one tile of NB KiB (4 rows each) from rows
     // following each other in memory; rows at or past `rows` read as zero
@@ -465,41 +481,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mod_kernel(BackwardParams p) { 
 __global__ __launch_bounds__(256, 2) void bwd_dq_d64_kernel(BackwardParams p) { bwd_dq_body<64, false>(p); }
 __global__ __launch_bounds__(256, 2) void bwd_dq_d64_mod_kernel(BackwardParams p) { bwd_dq_body<64, true>(p); }
 
-// dK and dV: each wave owns 32 keys (K and V fragments in registers) and
-// streams 64-row query tiles of every query head of its group.
+// dK and dV at d = 64: each wave owns 32 keys (K and V fragments in
+// registers) and streams 64-row query tiles of every query head of its group;
+// every Q and dO tile is copied twice, in the row and the transposed padded
+// layouts.  (At d = 128 the two-wave pass below runs instead.)
 // MODS: as for the dQ pass; each streamed tile's query head brings its own slope.
-//
-// SWZ (d = 128): each Q and dO tile sits in LDS once, unpadded (256-byte rows),
-// with 16-byte chunk c of row r stored at chunk c ^ (4 (r % 4) + (r / 4) % 4).
-// That one layout serves both reads without bank conflicts: 16 consecutive
-// rows at one chunk (the row operand) land in 16 different chunks, and the 4
-// consecutive rows x 64 bytes of a transposing read land in 16 different
-// chunks (checked on a CPU model of the banks).  Against the two padded
-// layouts it halves the copies and the LDS (66 KiB a workgroup against 150),
-// and every 1 KiB copy holds 4 whole rows with the same per-lane source offset
-// for all of a wave's copies.  (The pass still runs one workgroup per CU: its
-// dK/dV accumulators, K/V fragments, S and dP take about 380 registers.)
-// Backward of the causal 4x16x2048 prefill: 350 -> 330 us, same gradients.
-template <int D, bool MODS, bool SWZ>
+template <int D, bool MODS>
 __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     using C = PrefillBf16Cfg<D>;
     constexpr int BQ = 64;    // query rows per streamed tile
     constexpr int BK = 128;   // keys per workgroup
-    static_assert(!SWZ || D == 128, "the swizzled tiles are laid out for 256-byte rows");
-    constexpr int RT = SWZ ? BQ * D * 2 : C::KTILE;   // row-layout tile (the only tile with SWZ)
-    constexpr int TT = SWZ ? 16 : C::VTILE;           // transposed-layout tile (unused with SWZ)
-    __shared__ __attribute__((aligned(1024))) uint8_t qr0[RT];
-    __shared__ __attribute__((aligned(1024))) uint8_t qt0_[TT];
-    __shared__ __attribute__((aligned(1024))) uint8_t dr0[RT];
-    __shared__ __attribute__((aligned(1024))) uint8_t dt0_[TT];
-    __shared__ __attribute__((aligned(1024))) uint8_t qr1[RT];
-    __shared__ __attribute__((aligned(1024))) uint8_t qt1_[TT];
-    __shared__ __attribute__((aligned(1024))) uint8_t dr1[RT];
-    __shared__ __attribute__((aligned(1024))) uint8_t dt1_[TT];
-    uint8_t* qt0 = SWZ ? qr0 : qt0_;
-    uint8_t* dt0 = SWZ ? dr0 : dt0_;
-    uint8_t* qt1 = SWZ ? qr1 : qt1_;
-    uint8_t* dt1 = SWZ ? dr1 : dt1_;
+    __shared__ __attribute__((aligned(1024))) uint8_t qr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qt0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dt0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qr1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t qt1[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t dt1[C::VTILE];
     // per tile row: -LSE log2 e, D, lo, hi (256 bytes each)
     __shared__ __attribute__((aligned(1024))) uint8_t st0[4 * BQ * 4];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[4 * BQ * 4];
@@ -541,25 +540,17 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     const int n_iter = ntq * p.group;
 
     uint32_t koff[C::KLW], voff[C::VLW];
-    int kbase = 0, vbase = 0;
-    DualSwizzle dz;
-    if constexpr (SWZ) {
-        dz.init(lane, wave);
-    } else {
-        tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
-        tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
-        kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
-        vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-    }
+    tile_src_offsets<D, C::KS, C::KLOADS>(koff, wave, lane);
+    tile_src_offsets<D, C::VS, C::VLOADS>(voff, wave, lane);
+    const int kbase = (lane & 31) * C::KS * 16 + (lane >> 5) * 16;
+    const int vbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * C::VS * 16 + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
     // A operands: rows of a Q or dO tile (32-row block jb, head-dim step kk),
     // and a Q or dO tile transposed (16-row block kb, 32-column block cb)
     auto rowop = [&](const uint8_t* tile, int jb, int kk) __attribute__((always_inline)) {
-        if constexpr (SWZ) return dz.row(tile, jb, kk);
-        else return row_operand<D>(tile + kbase, jb, kk);
+        return row_operand<D>(tile + kbase, jb, kk);
     };
     auto trop = [&](const uint8_t* tile, int kb, int cb) __attribute__((always_inline)) {
-        if constexpr (SWZ) return dz.tr(tile, kb, cb);
-        else return tr_operand<D>(tile + vbase, kb, cb);
+        return tr_operand<D>(tile + vbase, kb, cb);
     };
 
     auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * p.group + it / ntq; };
@@ -571,18 +562,11 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
         const int q0 = q0_of(it);
         const uint16_t* qg = p.q + head_row * D;
         const uint16_t* dg = p.dO + head_row * D;
-        if constexpr (SWZ) {
-            // rows past Nq read as zero
-            dz.template copy<BQ / 4>(qg + (size_t)q0 * D, p.Nq - q0, qr, wave);
-            dz.template copy<BQ / 4>(dg + (size_t)q0 * D, p.Nq - q0, dr, wave);
-            (void)qt;
-            (void)dt;
-        } else {
-            load_tile_async<D, C::KS, C::KLOADS>(qg, q0, p.Nq, qr, koff, wave);
-            load_tile_async<D, C::VS, C::VLOADS>(qg, q0, p.Nq, qt, voff, wave);
-            load_tile_async<D, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
-            load_tile_async<D, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
-        }
+        // rows past Nq read as zero
+        load_tile_async<D, C::KS, C::KLOADS>(qg, q0, p.Nq, qr, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(qg, q0, p.Nq, qt, voff, wave);
+        load_tile_async<D, C::KS, C::KLOADS>(dg, q0, p.Nq, dr, koff, wave);
+        load_tile_async<D, C::VS, C::VLOADS>(dg, q0, p.Nq, dt, voff, wave);
         const int nrow = min(p.Nq - q0, BQ) * 4;   // bytes of the tile's rows that exist; the rest read 0
         const void* srcs[4] = {p.ws_nl + head_row + q0, p.ws_d + head_row + q0, p.ws_lo + head_row + q0,
                                p.ws_hi + head_row + q0};
@@ -764,10 +748,303 @@ __device__ __forceinline__ void bwd_dkdv_body(BackwardParams p) {
     }
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BackwardParams p) { bwd_dkdv_body<128, false, true>(p); }
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_mod_kernel(BackwardParams p) { bwd_dkdv_body<128, true, true>(p); }
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_kernel(BackwardParams p) { bwd_dkdv_body<64, false, false>(p); }
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_mod_kernel(BackwardParams p) { bwd_dkdv_body<64, true, false>(p); }
+
+// dK and dV at d = 128 with two waves per 32-key block, on one SIMD: wave A
+// (0-3) holds the block's K fragments and dV, wave B (4-7) its V fragments
+// and dK.  No product is computed twice, and each wave needs about half the
+// registers of one wave doing all four products, so two fit on a SIMD.  B
+// runs one query tile behind A, so the two waves' matrix and vector phases
+// alternate: at tile t,
+//   phase 1  A: S(t) = Q K^T                  B: dS(t-1) = P (dP - D)
+//   phase 2  A: P(t) = exp2(...), to LDS      B: dP(t) = dO V^T
+//   phase 3  A: dV^T += dO^T P(t)             B: dK^T += Q^T dS(t-1)
+// with P (times the cap factor under score modifications) handed from A
+// to B in LDS.  B still reads tile t-1 at tile t, so the ring has three
+// stages.
+template <bool MODS>
+__device__ __forceinline__ void bwd_dkdv2_body(BackwardParams p) {
+    constexpr int D = 128;
+    constexpr int BQ = 64;    // query rows per streamed tile
+    constexpr int BK = 128;   // keys per workgroup
+    constexpr int RT = BQ * D * 2;
+    constexpr int RB = 2 * D + 16;   // staged output row stride (bytes)
+    constexpr int PW = 32 * RB / 4;  // floats per key block in pbuf (the staging size: pbuf stages rows too)
+    __shared__ __attribute__((aligned(1024))) uint8_t qr0[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr0[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t qr1[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr1[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t qr2[RT];
+    __shared__ __attribute__((aligned(1024))) uint8_t dr2[RT];
+    // per tile row: -LSE log2 e, D, lo, hi (256 bytes each)
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[4 * BQ * 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[4 * BQ * 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[4 * BQ * 4];
+    // A's weights for B: 32 per lane and key block, element e of lane l at
+    // e / 4 * 256 + l * 4 + e % 4; after the loop, A's dV rows on their way out
+    __shared__ __attribute__((aligned(16))) float pbuf[4 * PW];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_a = wave < 4;
+    const int kw = wave & 3;
+    const int nbk = p.B * p.Hkv;
+    const int kt_idx = blockIdx.x / nbk;     // key tiles in order: under causal masks the first are the heaviest
+    const int bk = blockIdx.x % nbk;
+    const int b = bk / p.Hkv, hkv = bk % p.Hkv;
+    const PrefillParams m = mask_params(p);
+
+    const int k0 = kt_idx * BK;
+    const int k0w = k0 + kw * 32;
+    const int key = k0w + (lane & 31);
+    const bool key_ok = key < p.Nk;
+    const int k_last = min(k0 + BK, p.Nk) - 1;
+
+    const size_t kv_head = ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk;
+    bf16x8 xf[D / 16];   // A: K fragments, B: V fragments
+    load_fragment<D>((is_a ? p.k : p.v) + (kv_head + (key_ok ? key : 0)) * D, key_ok, lane, xf);
+    f32x16 acc[D / 32];  // A: dV^T, B: dK^T
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+
+    int first = p.Nq, last = -1;
+    if (k0 < p.Nk) query_rows_seeing(m, k0, k_last, first, last);
+    const int qt_first = first / BQ;
+    const int ntq = (first <= last && k0 < p.Nk) ? last / BQ - qt_first + 1 : 0;
+    const int n_iter = ntq * p.group;
+
+    DualSwizzle dz;
+    dz.init(lane, kw);
+    auto head_of = [&](int it) __attribute__((always_inline)) { return hkv * p.group + it / ntq; };
+    auto q0_of = [&](int it) __attribute__((always_inline)) { return (qt_first + it % ntq) * BQ; };
+    auto copy = [&](int it, uint8_t* qr, uint8_t* dr, uint8_t* st) __attribute__((always_inline)) {
+        const size_t head_row = ((size_t)b * p.Hq + head_of(it)) * (size_t)p.Nq;
+        const int q0 = q0_of(it);
+        // rows past Nq read as zero
+        dz.template copy8<BQ / 4>(p.q + (head_row + q0) * D, p.Nq - q0, qr, wave);
+        dz.template copy8<BQ / 4>(p.dO + (head_row + q0) * D, p.Nq - q0, dr, wave);
+        if (wave == 0) {
+            const int nrow = min(p.Nq - q0, BQ) * 4;   // bytes of the tile's rows that exist; the rest read 0
+            const void* srcs[4] = {p.ws_nl + head_row + q0, p.ws_d + head_row + q0, p.ws_lo + head_row + q0,
+                                   p.ws_hi + head_row + q0};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srcs[a], (short)0, nrow, 0x00020000);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + a * BQ * 4), 4, lane * 4, 0, 0, 0);
+            }
+        }
+    };
+    // does some row of tile it see some key of this block (its keys exist)?
+    auto tile_active = [&](int it, bool& full) __attribute__((always_inline)) {
+        const int q0 = q0_of(it);
+        const int q_end = min(q0 + BQ, p.Nq) - 1;
+        int lo_a, hi_a, lo_z, hi_z;
+        row_interval(m, q0, lo_a, hi_a);
+        row_interval(m, q_end, lo_z, hi_z);
+        full = q0 + BQ - 1 < p.Nq && k0w + 31 < p.Nk && hi_a >= k0w + 31 && (lo_z <= k0w || k0w + 31 < p.sink_end);
+        return k0w < p.Nk && hi_z >= k0w && (lo_a <= k0w + 31 || k0w < p.sink_end);
+    };
+    float* pw = pbuf + kw * PW;
+
+    // B: dS of the tile behind (dP in xr, statistics st) from A's weights, packed into pr
+    auto b_ds = [&](const uint8_t* st, f32x16 (&xr)[2], bf16x8 (&pr)[4]) __attribute__((always_inline)) {
+        const float* dd = (const float*)(st + BQ * 4);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int jb = q >> 2, r0 = 4 * (q & 3);
+            const int rb = jb * 32 + 8 * (q & 3) + 4 * (lane >> 5);
+            const f32x4 dd4 = *(const f32x4*)(dd + rb);
+            const f32x4 pa = *(const f32x4*)(pw + q * 256 + lane * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xr[jb][r0 + e] = pa[e] * (xr[jb][r0 + e] - dd4[e]);   // dS
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int jb = kb >> 1, h = (kb & 1) * 8;
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(xr[jb][h + 2 * e], xr[jb][h + 2 * e + 1]);
+            pr[kb] = __builtin_bit_cast(bf16x8, w);
+        }
+    };
+    // B: dK^T += Q^T dS of the tile behind (packed in pr; its Q tile qr)
+    auto b_dk = [&](const uint8_t* qr, const bf16x8 (&pr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dz.tr(qr, kb, cb), pr[kb], acc[cb], 0, 0, 0);
+    };
+
+    // The roles run loops of their own (the same copies and barriers in the
+    // same order), so each role's values count against its own registers only.
+    auto head = [&](int it, uint8_t* qrn, uint8_t* drn, uint8_t* stn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();   // tile it landed; A's weights of the tile behind are in LDS
+        if (it + 1 < n_iter) copy(it + 1, qrn, drn, stn);
+    };
+    // A: tile it in ring stage (qr, dr, st); the next tile's copies go to (qrn, drn, stn)
+    auto stage_a = [&](int it, const uint8_t* qr, const uint8_t* dr, const uint8_t* st, uint8_t* qrn, uint8_t* drn,
+                       uint8_t* stn) __attribute__((always_inline)) {
+        head(it, qrn, drn, stn);
+        bool full;
+        const bool active = tile_active(it, full);
+        const int q0 = q0_of(it);
+        f32x16 xr[2];     // S, then P
+        bf16x8 pr[4];     // P packed per 16-row block
+        // phase 1: S = Q K^T
+        if (active) {
+            xr[0] = f32x16{};
+            xr[1] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    xr[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dz.row(qr, jb, kk), xf[kk], xr[jb], 0, 0, 0);
+            order_operand_reads<D / 8, 1, 4>();
+        }
+        __syncthreads();   // B has read the weights of the tile behind
+        // phase 2: the weights, into LDS for B; phase 3: dV^T += dO^T P
+        if (active) {
+            f32x16 fac[2];
+            if constexpr (MODS) {
+                const ScoreMod sm = make_score_mod(p.scale_log2, p.softcap, p.alibi_slopes, head_of(it));
+                const float b0 = sm.slope_l2 * (float)(key - q0 - 4 * (lane >> 5) - p.Nk + p.Nq);
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float bias = __builtin_fmaf(-sm.slope_l2, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), b0);
+                        if (sm.cap_k != 0.f) {
+                            const float rr = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(xr[jb][r] * sm.cap_k) + 1.f);
+                            xr[jb][r] = __builtin_fmaf(-2.f * sm.cap_l2, rr, sm.cap_l2) + bias;
+                            fac[jb][r] = 4.f * rr * (1.f - rr);
+                        } else {
+                            xr[jb][r] = __builtin_fmaf(xr[jb][r], sm.scale_l2, bias);
+                            fac[jb][r] = 1.f;
+                        }
+                    }
+            }
+            const float sl = MODS ? 1.f : p.scale_log2;   // scores already in base-2 units under MODS
+            if (!full) {
+                // scores of invisible (row, key) pairs and of rows past Nq
+                // become -inf, so their P (and B's dS) are 0
+                const int32_t* rlo = (const int32_t*)(st + 2 * BQ * 4);
+                const int32_t* rhi = (const int32_t*)(st + 3 * BQ * 4);
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int rb = jb * 32 + 8 * g4 + 4 * (lane >> 5);
+                        const u32x4 a = *(const u32x4*)(rlo + rb);
+                        const u32x4 z = *(const u32x4*)(rhi + rb);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bool vis = q0 + rb + e < p.Nq && key <= (int32_t)z[e] &&
+                                             (key >= (int32_t)a[e] || key < p.sink_end);
+                            if (!vis) xr[jb][4 * g4 + e] = -__builtin_inff();
+                        }
+                    }
+            }
+            const float* nl = (const float*)st;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int rb = (q >> 2) * 32 + 8 * (q & 3) + 4 * (lane >> 5);
+                const f32x4 nl4 = *(const f32x4*)(nl + rb);
+                const int jb = q >> 2, r0 = 4 * (q & 3);
+                f32x4 hand;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xr[jb][r0 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xr[jb][r0 + e], sl, nl4[e]));   // P
+                    hand[e] = MODS ? xr[jb][r0 + e] * fac[jb][r0 + e] : xr[jb][r0 + e];
+                }
+                *(f32x4*)(pw + q * 256 + lane * 4) = hand;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int jb = kb >> 1, h = (kb & 1) * 8;
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(xr[jb][h + 2 * e], xr[jb][h + 2 * e + 1]);
+                pr[kb] = __builtin_bit_cast(bf16x8, w);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int cb = 0; cb < D / 32; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dz.tr(dr, kb, cb), pr[kb], acc[cb], 0, 0, 0);
+        }
+    };
+    // B: tile it in (dr, st), the tile behind in (qrp, stp); dP of the tile
+    // behind in xr, its dS packed into pr
+    bool b_pending = false;   // the tile behind needs its dS and dK
+    auto stage_b = [&](int it, const uint8_t* dr, const uint8_t* qrp, const uint8_t* stp, uint8_t* qrn,
+                       uint8_t* drn, uint8_t* stn, f32x16 (&xr)[2], bf16x8 (&pr)[4]) __attribute__((always_inline)) {
+        head(it, qrn, drn, stn);
+        bool full;
+        const bool active = tile_active(it, full);
+        // phase 1: dS of the tile behind
+        if (b_pending) b_ds(stp, xr, pr);
+        __syncthreads();   // B has read the weights of the tile behind
+        // phase 2: dP = dO V^T of this tile
+        if (active) {
+            xr[0] = f32x16{};
+            xr[1] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    xr[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dz.row(dr, jb, kk), xf[kk], xr[jb], 0, 0, 0);
+            order_operand_reads<D / 8, 1, 4>();
+        }
+        // phase 3: dK^T += Q^T dS of the tile behind
+        if (b_pending) b_dk(qrp, pr);
+        b_pending = active;
+    };
+
+    if (is_a) {
+        if (n_iter > 0) {
+            copy(0, qr0, dr0, st0);
+            for (int it = 0; it < n_iter; it += 3) {
+                stage_a(it, qr0, dr0, st0, qr1, dr1, st1);
+                if (it + 1 < n_iter) stage_a(it + 1, qr1, dr1, st1, qr2, dr2, st2);
+                if (it + 2 < n_iter) stage_a(it + 2, qr2, dr2, st2, qr0, dr0, st0);
+            }
+        }
+        __syncthreads();   // A's weights of the last tile are in LDS
+    } else {
+        f32x16 xr[2];
+        bf16x8 pr[4];
+        if (n_iter > 0) {
+            copy(0, qr0, dr0, st0);
+            for (int it = 0; it < n_iter; it += 3) {
+                stage_b(it, dr0, qr2, st2, qr1, dr1, st1, xr, pr);
+                if (it + 1 < n_iter) stage_b(it + 1, dr1, qr0, st0, qr2, dr2, st2, xr, pr);
+                if (it + 2 < n_iter) stage_b(it + 2, dr2, qr1, st1, qr0, dr0, st0, xr, pr);
+            }
+        }
+        __syncthreads();   // A's weights of the last tile are in LDS
+        // dS and dK of the last tile (ring stage (n_iter - 1) % 3)
+        if (b_pending) {
+            const int ls = (n_iter - 1) % 3;
+            b_ds(ls == 0 ? st0 : (ls == 1 ? st1 : st2), xr, pr);
+            b_dk(ls == 0 ? qr0 : (ls == 1 ? qr1 : qr2), pr);
+        }
+    }
+    __syncthreads();   // every wave is done with the ring and pbuf: both stage their rows there
+    if (k0w < p.Nk) {
+        if (is_a) {
+            store_rows_staged<D>(p.dv + (kv_head + k0w) * D, p.Nk - k0w, acc, 1.f, lane, (uint8_t*)pw);
+        } else {
+            uint8_t* stg = kw == 0 ? dr0 : (kw == 1 ? dr1 : (kw == 2 ? dr2 : qr0));
+            store_rows_staged<D>(p.dk + (kv_head + k0w) * D, p.Nk - k0w, acc, p.scale, lane, stg);
+        }
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void bwd_dkdv2_kernel(BackwardParams p) { bwd_dkdv2_body<false>(p); }
+__global__ __launch_bounds__(512, 1) void bwd_dkdv2_mod_kernel(BackwardParams p) { bwd_dkdv2_body<true>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_kernel(BackwardParams p) { bwd_dkdv_body<64, false>(p); }
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d64_mod_kernel(BackwardParams p) { bwd_dkdv_body<64, true>(p); }
 
 size_t backward_workspace_bytes(int B, int Hq, int Nq) {
     const size_t rows = (size_t)B * Hq * Nq;
@@ -797,8 +1074,9 @@ int launch_backward(BackwardParams p, int d, void* ws, hipStream_t stream) {
     launch_dsink(p, stream);   // after the dQ pass (it reads D); also with no rows, where it writes 0
     if ((long long)p.B * p.Hkv * p.num_k_tiles > 0) {
         if (d == 128) {
-            if (mods) hipLaunchKernelGGL(bwd_dkdv_mod_kernel, gk, wg, 0, stream, p);
-            else hipLaunchKernelGGL(bwd_dkdv_kernel, gk, wg, 0, stream, p);
+            const dim3 wg2(512);
+            if (mods) hipLaunchKernelGGL(bwd_dkdv2_mod_kernel, gk, wg2, 0, stream, p);
+            else hipLaunchKernelGGL(bwd_dkdv2_kernel, gk, wg2, 0, stream, p);
         } else {
             if (mods) hipLaunchKernelGGL(bwd_dkdv_d64_mod_kernel, gk, wg, 0, stream, p);
             else hipLaunchKernelGGL(bwd_dkdv_d64_kernel, gk, wg, 0, stream, p);

@@ -62,7 +62,7 @@ def test_pmc_plan_maps_dispatches_to_workloads():
              "decode_combine_kernel<128>": "void xattn::decode_combine_kernel<128>(xattn::DecodeParams)",
              "paged_prefill_swz_kernel<false>": "void xattn::paged_prefill_swz_kernel<false>(xattn::PagedPrefillParams)",
              "bwd_dq_kernel": "void xattn::bwd_dq_kernel(xattn::BwdParams)",
-             "bwd_dkdv_kernel": "void xattn::bwd_dkdv_kernel(xattn::BwdParams)"}
+             "bwd_dkdv2_kernel": "void xattn::bwd_dkdv2_kernel(xattn::BwdParams)"}
     per[(str(did), "__amd_rocclr_copyBuffer")] = 1.0
     for leg, n in bench.PMC_PLAN:
         for i in range(n):
