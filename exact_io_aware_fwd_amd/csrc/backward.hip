@@ -800,8 +800,13 @@ __device__ __forceinline__ void bwd_dkdv2_body(BackwardParams p) {
     const int k_last = min(k0 + BK, p.Nk) - 1;
 
     const size_t kv_head = ((size_t)b * p.Hkv + hkv) * (size_t)p.Nk;
-    bf16x8 xf[D / 16];   // A: K fragments, B: V fragments
-    load_fragment<D>((is_a ? p.k : p.v) + (kv_head + (key_ok ? key : 0)) * D, key_ok, lane, xf);
+    // A: K fragments, B: V fragments.  A key past Nk reads key 0's row and
+    // keeps it: its column of S is masked to -inf, so its P and dS are 0, and
+    // its dK and dV rows are never stored.  Not zeroing it lets the loads stay
+    // in flight while the first tile's copies are issued (the first wait is
+    // the first tile's).
+    bf16x8 xf[D / 16];
+    load_fragment<D>((is_a ? p.k : p.v) + (kv_head + (key_ok ? key : 0)) * D, true, lane, xf);
     f32x16 acc[D / 32];  // A: dV^T, B: dK^T
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};

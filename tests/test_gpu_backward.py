@@ -53,10 +53,13 @@ def run_case(c, label, sink_tokens=0, sinks=None, softcap=0.0, slopes=None):
                                     c["mask"], c["window"], c["doc_offsets"], sink_tokens,
                                     None if sinks is None else sinks.astype(np.float64), softcap=softcap,
                                     alibi_slopes=None if slopes is None else slopes.astype(np.float64))
+    grads = []
     for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
-        check_grad(host_f64(got), want, f"{label} {name}")
+        grads.append(host_f64(got))
+        check_grad(grads[-1], want, f"{label} {name}")
     if sinks is not None:
         check_grad(host_f64(ds), ref[3], f"{label} dsink")
+    return grads
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -90,6 +93,17 @@ def test_backward_ragged_and_aligned(Nq, Nk):
     # causal, bottom-right: Nq > Nk leaves the first rows with no key
     c = workloads.make_backward(2, 4, 2, Nq, Nk, 128, seed=73, mask="causal")
     run_case(c, f"bwd causal {Nq}x{Nk}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_keys_no_row_sees(d):
+    # window 50, bottom-right aligned: the 100 rows see only keys 851..999,
+    # so the first key blocks get no query tile at all (an empty loop) and
+    # their dK and dV rows must come out exactly zero
+    c = workloads.make_backward(1, 4, 2, 100, 1000, d, seed=95, mask="window", window=50)
+    _, dk, dv = run_case(c, f"bwd window50 100x1000 d{d}")
+    assert np.all(dk[:, :, :851] == 0.0) and np.all(dv[:, :, :851] == 0.0), "unseen keys must get zero gradients"
+    assert np.any(dk[:, :, 851:] != 0.0) and np.any(dv[:, :, 851:] != 0.0)
 
 
 @pytest.mark.parametrize("sink_tokens,with_logits", [(4, True), (70, False), (0, True)])
