@@ -16,6 +16,9 @@ stream; the median, p10 and p90 of the per-call times are reported.  The legs
 are the five prefill workloads' four bf16 ones (C2 causal 4x16x2048, C3a GQA
 causal 8192, C3b GQA window-1024 8192, C4 document 32768), the paged decode
 (C5), the chunked prefill over the paged cache (C6) and the backward of C2.
+Beside the decode leg, a standalone streaming-read probe (_build/hbm_read_probe,
+built with the library) reads the same number of bytes once, as the practical
+read rate next to the published HBM peak (`--no-read-ceiling` skips it).
 
 Prints ONE JSON line.  `value` is the C2 prefill's algorithmic TFLOP/s
 (4·d·B·Hq·visible pairs per call ÷ the median call time); the other legs are
@@ -48,6 +51,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -87,6 +91,27 @@ CSRC = os.path.join(ROOT, "exact_io_aware_fwd_amd", "csrc")
 COPY_BYTES = 1 << 30          # known-size copy used to calibrate the HBM byte counters
 LEG_CALLS = 100               # timed calls per leg (at least)
 LEG_WARMUP = 10
+
+
+def read_ceiling(nbytes: int):
+    """The practical HBM read rate beside the published peak: the standalone
+    streaming-read probe (built with the library into _build/) reads a buffer
+    of the decode call's byte count linearly and as 4 KiB pages in a random
+    order; the best median of each pattern over a small sweep of grids, loads
+    in flight and load kinds.  None when the probe is not built or fails."""
+    exe = os.path.join(ROOT, "_build", "hbm_read_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, str(int(nbytes))], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        log("read-ceiling probe timed out")
+        return None
+    if r.returncode != 0:
+        log(f"read-ceiling probe failed: {r.stderr.strip()[-200:]}")
+        return None
+    lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
 
 
 def log(msg: str) -> None:
@@ -397,6 +422,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--calls", type=int, default=LEG_CALLS, help="timed calls per leg (at least 100 kept)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe beside the decode leg")
     ap.add_argument("--legs", default="c3a,c3b,c4,c6,bwd_c2",
                     help="legs timed beside C2 and C5 (comma list of c3a,c3b,c4,c6,bwd_c2; empty for none)")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -465,6 +491,20 @@ def main() -> int:
                               f"{int(dec.c['seq_lens'].sum())} cached tokens)",
                   "kernel": " + ".join(LEG_KERNELS["c5"]) + " (one call)", "bytes_per_call": dec.bytes, "us": d_st,
                   "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("c5")}
+    ceiling = None if args.no_read_ceiling else read_ceiling(dec.bytes)
+    if ceiling is not None:
+        lin, pg = ceiling["linear"], ceiling["pages"]
+        log(f"read ceiling over {ceiling['bytes']} bytes: linear {lin['median_gbs']:.1f} GB/s, 4 KiB pages in "
+            f"random order {pg['median_gbs']:.1f} GB/s (decode at {gbs / pg['median_gbs']:.3f} of the latter)")
+        legs["c5"]["read_ceiling"] = {
+            "pages_gbs": pg["median_gbs"], "linear_gbs": lin["median_gbs"],
+            "decode_frac_of_pages": round(gbs / pg["median_gbs"], 4),
+            "decode_frac_of_linear": round(gbs / lin["median_gbs"], 4),
+            "probe": "_build/hbm_read_probe: the same byte count read once with 16-byte loads, linearly and as "
+                     "4 KiB pages in a seeded random order; best median of each over grids, loads in flight and "
+                     f"load kinds (pages: {pg['grid']} workgroups, {pg['pages_in_flight_per_wave']} pages in flight "
+                     f"per wave, nontemporal {pg['nontemporal']}; linear: {lin['grid']} workgroups, "
+                     f"{lin['loads_in_flight_per_lane']} loads in flight per lane, nontemporal {lin['nontemporal']})"}
     extra = [x for x in args.legs.split(",") if x]
     if "bwd_c2" in extra:
         bwd = Backward(pre)
@@ -520,6 +560,7 @@ def main() -> int:
             "value": legs["c5"]["gbs"], "unit": "GB/s", "pct_of_peak": round(100 * legs["c5"]["frac"], 2),
             "roofline": {"bound": "hbm", "achieved": legs["c5"]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": legs["c5"]["frac"], "traffic": legs["c5"]["traffic"], "kernel": legs["c5"]["kernel"]},
+            "read_ceiling": legs["c5"].get("read_ceiling"),
         },
         "legs": legs,
     }

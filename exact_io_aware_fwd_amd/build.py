@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libexact_attn.so")
+# a standalone streaming-read probe (the practical HBM read rate beside the
+# published peak); not part of the library
+PROBE_SRC = os.path.join(CSRC, "hbm_read_probe.hip")
+PROBE = os.path.join(BUILD, "hbm_read_probe")
 SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "backward_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -52,6 +56,8 @@ def build(debug: bool = False, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    _run([HIPCC, *COMMON, "-O3", PROBE_SRC, "-o", PROBE + ".tmp"])
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
