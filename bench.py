@@ -73,7 +73,7 @@ PREFILL_LEGS = {"c2": "c2_causal_b4h16n2048", "c3a": "c3a_gqa_causal_n8192",
 # kernels each leg launches, once per call, in launch order
 LEG_KERNELS = {
     "c2": ["prefill_bf16_kernel<128, false>"], "c3a": ["prefill_bf16_kernel<128, false>"],
-    "c3b": ["prefill_bf16_kernel<128, false>"], "c4": ["prefill_bf16_kernel<128, false>"],
+    "c3b": ["prefill_bf16_k32_kernel<false>"], "c4": ["prefill_bf16_k32_kernel<false>"],
     "c5": ["decode_split_kernel<128, false>", "decode_combine_kernel<128>"],
     "c6": ["paged_prefill_swz_kernel<false>"],
     "bwd_c2": ["bwd_dq_kernel", "bwd_dkdv2_kernel"],

@@ -58,6 +58,7 @@ def test_pmc_plan_maps_dispatches_to_workloads():
     per = {}
     did = 0
     names = {"prefill_bf16_kernel<128, false>": "void xattn::prefill_bf16_kernel<128, false>(xattn::PrefillParams)",
+             "prefill_bf16_k32_kernel<false>": "void xattn::prefill_bf16_k32_kernel<false>(xattn::PrefillParams)",
              "decode_split_kernel<128, false>": "void xattn::decode_split_kernel<128, false>(xattn::DecodeParams)",
              "decode_combine_kernel<128>": "void xattn::decode_combine_kernel<128>(xattn::DecodeParams)",
              "paged_prefill_swz_kernel<false>": "void xattn::paged_prefill_swz_kernel<false>(xattn::PagedPrefillParams)",
@@ -75,6 +76,7 @@ def test_pmc_plan_maps_dispatches_to_workloads():
     assert set(got) == {leg for leg, _ in bench.PMC_PLAN}
     assert len(got["c3a"]["prefill_bf16_kernel<128, false>"]) == 2
     assert got["c2"]["prefill_bf16_kernel<128, false>"][0] == 100.0     # the first dispatch of the pass
+    assert set(got["c4"]) == {"prefill_bf16_k32_kernel<false>"}         # window and document legs
     assert all(v > 0 for leg in got.values() for vals in leg.values() for v in vals)
     del per[max(per, key=lambda k: int(k[0]) if "bwd_dkdv" in k[1] else -1)]
     with pytest.raises(SystemExit):
