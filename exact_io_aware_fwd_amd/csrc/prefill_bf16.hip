@@ -860,8 +860,11 @@ __device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
 
     const int32_t* bt = pp.block_table + (size_t)seq * pp.max_pages;
     const int last_page = max((L + 15) / 16 - 1, 0);
-    [[maybe_unused]] const size_t head_off = (size_t)hkv * 16 * D;
-    [[maybe_unused]] const size_t page_elems = (size_t)pp.Hkv * 16 * D;
+    // this KV head's rows in page 0 of the pool, and the bytes from one page
+    // to the next (a 32-bit count: Hkv * 16 rows * 256 bytes)
+    [[maybe_unused]] const uint8_t* kpool = (const uint8_t*)(pp.k_pages + (size_t)hkv * 16 * D);
+    [[maybe_unused]] const uint8_t* vpool = (const uint8_t*)(pp.v_pages + (size_t)hkv * 16 * D);
+    [[maybe_unused]] const uint32_t page_bytes = (uint32_t)pp.Hkv * (16u * D * 2u);
     struct Pages { int32_t e0, e1, e2, e3; };
     auto entries = [&](int t) __attribute__((always_inline)) {
         const int lp = t * (C::BN / 16);
@@ -872,19 +875,37 @@ __device__ __forceinline__ void paged_prefill_swz_body(PagedPrefillParams pp) {
         pg.e3 = bt[min(lp + 3, last_page)];
         return pg;
     };
+    // Page entries are valid page indices (non-negative), so a page's byte
+    // offset is one unsigned 32 x 32 -> 64-bit product.  A tile whose 64 keys
+    // all exist (every tile but a sequence's last) takes whole-page ranges;
+    // only the last tile clamps each page's range to its rows that exist.
+    auto copy_pages = [&](const int32_t (&e)[4], const int (&rows)[4], uint8_t* kd, uint8_t* vd)
+        __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const uint64_t off = (uint64_t)(uint32_t)e[jj] * page_bytes;
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kpool + off), (short)0, rows[jj] * D * 2, 0x00020000);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vpool + off), (short)0, rows[jj] * D * 2, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + (4 * jj + wave) * 1024), 16, kvo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + (4 * jj + wave) * 1024), 16, vvo, 0, 0, 0);
+        }
+#endif
+    };
     auto copy_tile = [&](int t, const Pages& pg, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
         const int32_t e[4] = {__builtin_amdgcn_readfirstlane(pg.e0), __builtin_amdgcn_readfirstlane(pg.e1),
                               __builtin_amdgcn_readfirstlane(pg.e2), __builtin_amdgcn_readfirstlane(pg.e3)};
+        const int left = L - t * C::BN;   // keys from this tile's first to the sequence's end (uniform)
+        if (left >= C::BN) {
+            const int rows[4] = {16, 16, 16, 16};
+            copy_pages(e, rows, kd, vd);
+        } else {
+            // rows of each page that exist (uniform, so the resources stay scalar)
+            int rows[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            // rows of this page that exist (uniform, so the resource stays scalar)
-            const int valid = __builtin_amdgcn_readfirstlane(min(max(L - (t * C::BN + 16 * jj), 0), 16));
-            const size_t off = (size_t)e[jj] * page_elems + head_off;
-            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(pp.k_pages + off), (short)0, valid * D * 2, 0x00020000);
-            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(pp.v_pages + off), (short)0, valid * D * 2, 0x00020000);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + (4 * jj + wave) * 1024), 16, kvo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + (4 * jj + wave) * 1024), 16, vvo, 0, 0, 0);
+            for (int jj = 0; jj < 4; ++jj) rows[jj] = __builtin_amdgcn_readfirstlane(min(max(left - 16 * jj, 0), 16));
+            copy_pages(e, rows, kd, vd);
         }
 #endif
     };

@@ -45,22 +45,22 @@ def inputs():
     return q.to(torch.bfloat16), k, v
 
 
-def expected(last_key: int):
-    """Output row and LSE of a query that sees keys 0..last_key."""
-    n = last_key + 1
+def expected(last_key: int, first_key: int = 0):
+    """Output row and LSE of a query that sees keys first_key..last_key."""
+    n = last_key - first_key + 1
     o = np.zeros(D)
     for a, b, col, val in MARKS:
-        seen = max(0, min(b, last_key) - a + 1)
+        seen = max(0, min(b, last_key) - max(a, first_key) + 1)
         o[col] += val * seen / n
     return o, math.log(n)
 
 
-def check(o: torch.Tensor, lse: torch.Tensor, last_keys, label: str):
+def check(o: torch.Tensor, lse: torch.Tensor, last_keys, label: str, first_keys=None):
     og = o[0].double().cpu().numpy()      # [Hq, NQ, D]
     lg = lse[0].double().cpu().numpy()    # [Hq, NQ]
     worst_rel, worst_lse = 0.0, 0.0
     for i, lk in enumerate(last_keys):
-        o_ref, l_ref = expected(lk)
+        o_ref, l_ref = expected(lk, 0 if first_keys is None else first_keys[i])
         nz = o_ref != 0
         for h in range(og.shape[0]):
             assert np.all(og[h, i, ~nz] == 0.0), f"{label} row {i}: nonzero output where V is zero"
@@ -84,6 +84,27 @@ def test_prefill_keys_past_2_24_causal_bottom_right():
     o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="causal")
     torch.cuda.synchronize()
     check(o, lse, [NK - NQ + i for i in range(NQ)], "causal")
+
+
+def test_prefill_keys_past_2_24_window_as_wide_as_the_keys():
+    """A window of all the keys is the bottom-right causal mask; the window
+    mask runs on the 32-key-tile kernel."""
+    q, k, v = inputs()
+    o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="window", window=NK)
+    torch.cuda.synchronize()
+    check(o, lse, [NK - NQ + i for i in range(NQ)], "window of all keys (32-key tiles)")
+
+
+def test_prefill_keys_past_2_24_window_edge_through_a_mark():
+    """Window 2^23 - 50: row i (position NK - NQ + i) sees keys from
+    position - W + 1, an edge that sweeps through the marked rows just past
+    2^23 as i grows, inside 32-key tiles whose byte offsets pass 2^31."""
+    W = (1 << 23) - 50
+    q, k, v = inputs()
+    o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(D), mask="window", window=W)
+    torch.cuda.synchronize()
+    pos = [NK - NQ + i for i in range(NQ)]
+    check(o, lse, pos, "window 2^23 - 50 (32-key tiles)", first_keys=[p - W + 1 for p in pos])
 
 
 def test_backward_rows_past_2_24():
